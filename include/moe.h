@@ -1,0 +1,156 @@
+/* moe.h -- C ABI of the MI355X (gfx950) MoE-layer library (libmoe_mi355x.so).
+ *
+ * One DeepSeek-V3-style mixture-of-experts layer, forward and backward, computed in MXFP8 on
+ * one GPU with every expert resident in HBM.  The method is the one the pages describe for
+ * Cursor's Mixture-of-Kittens training megakernel (knowledge card
+ * "Mixture-of-Kittens——面向NVL72的开源MoE训练megakernel", sections 一句话结论 and
+ * 方法/产品要点; article "Cursor 為 Composer 改造 MoE 訓練：MoK 點樣拆走跨 GPU 樽頸", section
+ * "MoK 將運算同通訊塞入同一個核心"): a device-side schedule reused by the backward pass,
+ * pull-based dispatch, push-based combine, pull-based reverse-combine, push-based
+ * reverse-dispatch, fixed-capacity ring token buffers, no CPU-GPU synchronisation inside the
+ * layer, deterministic results.
+ *
+ * Conventions for every entry point
+ *   - Pointers are device pointers unless stated otherwise; the caller allocates and frees
+ *     every buffer.  The library never allocates device memory, never frees, and never
+ *     synchronises the host: work is enqueued on the caller's stream and the call returns.
+ *   - Tensors are dense, row-major, contiguous.  "bf16" is bfloat16 stored as uint16_t,
+ *     "fp8" is OCP e4m3 ("fn") stored as uint8_t, "e8m0" is a biased-127 exponent byte.
+ *   - MXFP8: a tensor quantised along an axis holds fp8 codes of the same shape plus one
+ *     e8m0 byte per 32 consecutive values along that axis (OCP Microscaling v1.0).
+ *   - Argument errors are detected on the host before anything is enqueued and returned as a
+ *     moe_status; nothing is launched then.  Launch failures return MOE_ELAUNCH.
+ *   - Tensor pointers must be 16-byte aligned; `saved` and `workspace` 256-byte aligned.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,      /* null pointer or unsupported option */
+  MOE_ESHAPE = 2,      /* sizes outside the supported set (see moe_config) */
+  MOE_EALIGN = 3,      /* a pointer is not aligned as required */
+  MOE_EWORKSPACE = 4,  /* reserved: workspace smaller than moe_query reports */
+  MOE_ELAUNCH = 5,     /* a kernel launch failed */
+  MOE_EDEVICE = 6      /* reported by moe_device_status: the device flagged an anomaly */
+} moe_status;
+
+typedef enum moe_score_fn {
+  MOE_SCORE_SOFTMAX = 0, /* softmax over the k selected logits */
+  MOE_SCORE_SIGMOID = 1  /* sigmoid scores of the k selected experts, normalised to sum 1 */
+} moe_score_fn;
+
+/* Layer shape and tuning.  Supported: T >= 1; d and inter multiples of 128; 1 <= k <= 16;
+ * k <= E <= 512; n_shared in {0, 1}.  The tuning fields (ring_rows, chunk_rows, producer_wgs)
+ * correspond to the pages' per-workload knobs (buffer capacity, minibatch and number of
+ * communication SMs: article section "2.37 倍同 1.41 倍係兩份成績"); 0 picks a default.  They
+ * never change results. */
+typedef struct moe_config {
+  int32_t T;          /* tokens */
+  int32_t d;          /* hidden size */
+  int32_t E;          /* routed experts */
+  int32_t k;          /* experts per token */
+  int32_t inter;      /* SwiGLU intermediate size I */
+  int32_t n_shared;   /* always-on shared experts (weight 1), stored after the E routed ones */
+  int32_t score_fn;   /* moe_score_fn */
+  int32_t ring_rows;  /* ring token buffer capacity in rows (0 = default) */
+  int32_t chunk_rows; /* rows per ring chunk (0 = default) */
+  int32_t producer_wgs; /* gather (producer) workgroups of the persistent dispatch kernel (0 = default) */
+  uint32_t flags;     /* MOE_F_* */
+} moe_config;
+
+/* MOE_F_DIRECT_GATHER: the forward gate/up GEMM pulls its rows straight from the quantised
+ * activations instead of through the ring token buffer (same results; a measurement switch). */
+#define MOE_F_DIRECT_GATHER 1u
+
+/* Byte offsets inside the caller-owned `saved` buffer that moe_fwd fills and moe_bwd reads
+ * (the schedule is built once and reused by the backward pass).  R = T*k routed rows,
+ * RS = R + n_shared*T rows in expert-major ("permuted") order, S = n_shared, NX = E + S. */
+typedef struct moe_saved_layout {
+  size_t logits;     /* float [T, E]       router logits (+ bias) */
+  size_t idx;        /* int32 [T, k]       selected experts, best first */
+  size_t w;          /* float [T, k]       combine weights */
+  size_t counts;     /* int32 [NX]         rows per expert */
+  size_t offsets;    /* int32 [NX + 1]     first permuted row of each expert */
+  size_t poffsets;   /* int32 [NX + 1]     offsets with every count rounded up to 32 */
+  size_t tok_off;    /* int64 [NX + 1]     offsets with every count rounded up to 128 */
+  size_t tile_start; /* int32 [NX + 1]     first 128-row tile of each expert */
+  size_t tile64;     /* int32 [NX + 1]     first 64-row tile of each 128-padded segment */
+  size_t perm;       /* int32 [R]          slot id t*k + j of each routed permuted row */
+  size_t pos;        /* int32 [T, k]       permuted row of slot (t, j) */
+  size_t xq;         /* fp8   [T, d]       x quantised along d */
+  size_t xs;         /* e8m0  [T, d/32] */
+  size_t g;          /* float [RS, I]      gate pre-activations */
+  size_t u;          /* float [RS, I]      up projections */
+  size_t hq;         /* fp8   [RS, I]      silu(g) * u quantised along I */
+  size_t hs;         /* e8m0  [RS, I/32] */
+  size_t yslot;      /* float [T, k + S, d] expert output of every (token, slot) */
+  size_t total;      /* bytes of `saved` */
+} moe_saved_layout;
+
+/* Sizes of the caller-owned buffers for `cfg`: *workspace_bytes for the workspace shared by
+ * moe_fwd and moe_bwd, *saved for the layout of the saved buffer.  Host-only; no GPU needed. */
+moe_status moe_query(const moe_config* cfg, size_t* workspace_bytes, moe_saved_layout* saved);
+
+/* MXFP8 quantisation of a [rows, cols] matrix along its contiguous axis (cols % 32 == 0):
+ * src is bf16 (src_is_f32 = 0) or float32 (src_is_f32 = 1); q [rows, cols] fp8 and
+ * scales [rows, cols/32] e8m0 receive the result.  Block scale 2^(floor(log2 amax) - 8), codes
+ * rounded to nearest even and saturated at +-448 (the format the pages name: knowledge card,
+ * 方法/产品要点, "MXFP8").  Used for expert weights and by the layer for x and dy. */
+moe_status moe_quantize_mxfp8(const void* src, int src_is_f32, int64_t rows, int64_t cols, uint8_t* q,
+                              uint8_t* scales, hipStream_t stream);
+
+/* Transposed requantisation: q [batch, rows, cols] fp8 with scales [batch, rows, cols/32]
+ * (quantised along cols) is dequantised exactly and quantised again along rows into
+ * qt [batch, cols, rows] with st [batch, cols, rows/32].  rows and cols multiples of 64.
+ * This is the backward pass's requantisation of transposed operands, applied by moe_bwd to
+ * the expert weights; exported for tests. */
+moe_status moe_requant_transpose(const uint8_t* q, const uint8_t* scales, int64_t batch, int64_t rows, int64_t cols,
+                                 uint8_t* qt, uint8_t* st, hipStream_t stream);
+
+/* Forward pass.
+ *   x [T, d] bf16; w_router [E, d] bf16; router_bias [E] float or NULL (added to every
+ *   token's logits); w1q [NX, 2I, d] fp8 with w1s [NX, 2I, d/32] (gate rows 0..I-1, up rows
+ *   I..2I-1, quantised along d); w2q [NX, d, I] fp8 with w2s [NX, d, I/32] (quantised along I).
+ *   Outputs: y_bf16 [T, d]; y_f32 [T, d] float or NULL (the same sum before bf16 rounding);
+ *   saved (moe_saved_layout) for moe_bwd.  workspace: moe_query's size.
+ * Steps (all on `stream`, no host sync): quantise x; router logits; top-k and weights; schedule
+ * (counts, offsets, stable expert-major permutation); gate/up grouped GEMM with rows pulled
+ * through the schedule, SwiGLU and H quantisation in the epilogue; down grouped GEMM pushing
+ * each row to its (token, slot); combine in fixed slot order. */
+moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, const float* router_bias,
+                   const uint8_t* w1q, const uint8_t* w1s, const uint8_t* w2q, const uint8_t* w2s, void* y_bf16,
+                   float* y_f32, void* saved, void* workspace, hipStream_t stream);
+
+/* Backward pass for upstream gradient dy [T, d] bf16, reusing `saved` from moe_fwd of the same
+ * inputs.  Outputs: dx_bf16 [T, d] and dx_f32 [T, d] float (or NULL); dw_router [E, d] float;
+ * dw1 [NX, 2I, d] float and dw2 [NX, d, I] float (same layouts as w1q / w2q).
+ * Steps: quantise dy; combine-weight and router gradients; transposed requantisation of the
+ * expert weights; dgrad of the down GEMM (rows pulled from dy: reverse-combine) with the SwiGLU
+ * backward and quantisation along 2I; dgrad of the gate/up GEMM pushing rows to their
+ * (token, slot) (reverse-dispatch); fixed-order reduction of dx; token-axis requantisation of
+ * the wgrad operands; weight-gradient GEMMs. */
+moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const void* w_router, const uint8_t* w1q,
+                   const uint8_t* w1s, const uint8_t* w2q, const uint8_t* w2s, const void* saved, void* dx_bf16,
+                   float* dx_f32, float* dw_router, float* dw1, float* dw2, void* workspace, hipStream_t stream);
+
+/* Reads the device status word of `workspace` (0 = fine) into *device_code.  Blocking copy:
+ * call after the caller has synchronised the stream.  Returns MOE_EDEVICE if the code is
+ * non-zero. */
+moe_status moe_device_status(const void* workspace, int32_t* device_code);
+
+/* Static text for a status. */
+const char* moe_strerror(moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

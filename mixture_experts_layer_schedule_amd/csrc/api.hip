@@ -1,0 +1,374 @@
+// Host side of the C ABI: validation, buffer layout, kernel sequence.  Nothing here blocks the
+// host or allocates device memory; every launch goes to the caller's stream.
+#include <mutex>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr size_t kAlign = 256;
+
+size_t up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Dims {
+  int64_t T, d, E, k, I, S, NX, R, RS, nblk, ld_tok, tiles_bound, tile64_bound;
+};
+
+Dims dims(const moe_config& c) {
+  Dims m;
+  m.T = c.T; m.d = c.d; m.E = c.E; m.k = c.k; m.I = c.inter; m.S = c.n_shared;
+  m.NX = m.E + m.S;
+  m.R = m.T * m.k;
+  m.RS = m.R + m.S * m.T;
+  m.nblk = (m.T + 255) / 256;
+  m.ld_tok = (int64_t)up((size_t)(m.RS + 127 * m.NX), 128);
+  m.tiles_bound = m.RS / 128 + m.NX + 1;
+  m.tile64_bound = m.ld_tok / 64;
+  return m;
+}
+
+moe_status check_config(const moe_config* c) {
+  if (!c) return MOE_EINVAL;
+  if (c->T < 1 || c->d < 128 || c->d % 128 || c->inter < 128 || c->inter % 128) return MOE_ESHAPE;
+  if (c->k < 1 || c->k > 16 || c->E < c->k || c->E > 512) return MOE_ESHAPE;
+  if (c->n_shared < 0 || c->n_shared > 1) return MOE_ESHAPE;
+  if (c->score_fn != MOE_SCORE_SOFTMAX && c->score_fn != MOE_SCORE_SIGMOID) return MOE_EINVAL;
+  if (c->ring_rows < 0 || c->chunk_rows < 0 || c->producer_wgs < 0) return MOE_ESHAPE;
+  if ((int64_t)c->T * c->k + (int64_t)c->n_shared * c->T >= (1ll << 30)) return MOE_ESHAPE;
+  return MOE_OK;
+}
+
+// Sequential layout builder.
+struct Layout {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    size_t o = off;
+    off = up(off + bytes, kAlign);
+    return o;
+  }
+};
+
+moe_saved_layout saved_layout(const Dims& m) {
+  moe_saved_layout s{};
+  Layout L;
+  s.logits = L.take(4 * m.T * m.E);
+  s.idx = L.take(4 * m.T * m.k);
+  s.w = L.take(4 * m.T * m.k);
+  s.counts = L.take(4 * m.NX);
+  s.offsets = L.take(4 * (m.NX + 1));
+  s.poffsets = L.take(4 * (m.NX + 1));
+  s.tok_off = L.take(8 * (m.NX + 1));
+  s.tile_start = L.take(4 * (m.NX + 1));
+  s.tile64 = L.take(4 * (m.NX + 1));
+  s.perm = L.take(4 * m.R);
+  s.pos = L.take(4 * m.R);
+  s.xq = L.take(m.T * m.d);
+  s.xs = L.take(m.T * m.d / 32);
+  s.g = L.take(4 * m.RS * m.I);
+  s.u = L.take(4 * m.RS * m.I);
+  s.hq = L.take(m.RS * m.I);
+  s.hs = L.take(m.RS * m.I / 32);
+  s.yslot = L.take(4 * m.T * (m.k + m.S) * m.d);
+  s.total = L.off;
+  return s;
+}
+
+struct Work {
+  size_t status, blkcnt, dyq, dys, dw, dl, w1tq, w1ts, w2tq, w2ts, dguq, dgus, dxslot;
+  size_t xt, xts, ht, hts, dyt, dyts, dgut, dguts, total;
+};
+
+Work work_layout(const Dims& m) {
+  Work w{};
+  Layout L;
+  w.status = L.take(64);
+  w.blkcnt = L.take(4 * m.nblk * m.E);
+  w.dyq = L.take(m.T * m.d);
+  w.dys = L.take(m.T * m.d / 32);
+  w.dw = L.take(4 * m.T * m.k);
+  w.dl = L.take(4 * m.T * m.k);
+  w.w1tq = L.take(m.NX * m.d * 2 * m.I);
+  w.w1ts = L.take(m.NX * m.d * 2 * m.I / 32);
+  w.w2tq = L.take(m.NX * m.I * m.d);
+  w.w2ts = L.take(m.NX * m.I * m.d / 32);
+  w.dguq = L.take(m.RS * 2 * m.I);
+  w.dgus = L.take(m.RS * 2 * m.I / 32);
+  w.dxslot = L.take(4 * m.T * (m.k + m.S) * m.d);
+  w.xt = L.take(m.d * m.ld_tok);
+  w.xts = L.take(m.d * m.ld_tok / 32);
+  w.ht = L.take(m.I * m.ld_tok);
+  w.hts = L.take(m.I * m.ld_tok / 32);
+  w.dyt = L.take(m.d * m.ld_tok);
+  w.dyts = L.take(m.d * m.ld_tok / 32);
+  w.dgut = L.take(2 * m.I * m.ld_tok);
+  w.dguts = L.take(2 * m.I * m.ld_tok / 32);
+  w.total = L.off;
+  return w;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+template <class T>
+T* at(void* base, size_t off) { return (T*)((char*)base + off); }
+template <class T>
+const T* at(const void* base, size_t off) { return (const T*)((const char*)base + off); }
+
+std::once_flag g_init_once;
+hipError_t g_init_err = hipSuccess;
+
+moe_status ensure_init() {
+  std::call_once(g_init_once, [] { g_init_err = gemm_init(); });
+  return g_init_err == hipSuccess ? MOE_OK : MOE_ELAUNCH;
+}
+
+#define MOE_TRY(expr)                      \
+  do {                                     \
+    if ((expr) != hipSuccess) return MOE_ELAUNCH; \
+  } while (0)
+
+SchedView sched_view(const void* saved, const moe_saved_layout& sl, const Dims& m) {
+  SchedView v;
+  v.perm = at<int32_t>(saved, sl.perm);
+  v.offsets = at<int32_t>(saved, sl.offsets);
+  v.tile_start = at<int32_t>(saved, sl.tile_start);
+  v.n_exp = (int)m.NX;
+  v.R = (int)m.R;
+  v.T = (int)m.T;
+  v.k = (int)m.k;
+  v.S = (int)m.S;
+  return v;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_query(const moe_config* cfg, size_t* workspace_bytes, moe_saved_layout* saved) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  Dims m = dims(*cfg);
+  if (workspace_bytes) *workspace_bytes = work_layout(m).total;
+  if (saved) *saved = saved_layout(m);
+  return MOE_OK;
+}
+
+moe_status moe_quantize_mxfp8(const void* src, int src_is_f32, int64_t rows, int64_t cols, uint8_t* q,
+                              uint8_t* scales, hipStream_t stream) {
+  if (!src || !q || !scales) return MOE_EINVAL;
+  if (rows < 0 || cols < 0 || cols % 32) return MOE_ESHAPE;
+  if (!aligned(src, 16) || !aligned(q, 16)) return MOE_EALIGN;
+  return launch_quant_rows(src, src_is_f32 ? 1 : 0, rows, cols, q, scales, stream) == hipSuccess ? MOE_OK
+                                                                                                : MOE_ELAUNCH;
+}
+
+moe_status moe_requant_transpose(const uint8_t* q, const uint8_t* scales, int64_t batch, int64_t rows, int64_t cols,
+                                 uint8_t* qt, uint8_t* st, hipStream_t stream) {
+  if (!q || !scales || !qt || !st) return MOE_EINVAL;
+  if (batch < 0 || rows < 0 || cols < 0 || rows % 64 || cols % 64) return MOE_ESHAPE;
+  if (!aligned(q, 16) || !aligned(qt, 16)) return MOE_EALIGN;
+  return launch_requant_t(q, scales, batch, rows, cols, qt, st, stream) == hipSuccess ? MOE_OK : MOE_ELAUNCH;
+}
+
+moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, const float* router_bias,
+                   const uint8_t* w1q, const uint8_t* w1s, const uint8_t* w2q, const uint8_t* w2s, void* y_bf16,
+                   float* y_f32, void* saved, void* workspace, hipStream_t stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!x || !w_router || !w1q || !w1s || !w2q || !w2s || !y_bf16 || !saved || !workspace) return MOE_EINVAL;
+  if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(w1q, 16) || !aligned(w2q, 16) || !aligned(y_bf16, 16) ||
+      (y_f32 && !aligned(y_f32, 16)) || !aligned(saved, kAlign) || !aligned(workspace, kAlign))
+    return MOE_EALIGN;
+  if ((st = ensure_init()) != MOE_OK) return st;
+  const Dims m = dims(*cfg);
+  const moe_saved_layout sl = saved_layout(m);
+  const Work wl = work_layout(m);
+  const int d = (int)m.d, I = (int)m.I;
+
+  uint8_t* xq = at<uint8_t>(saved, sl.xq);
+  uint8_t* xs = at<uint8_t>(saved, sl.xs);
+  float* logits = at<float>(saved, sl.logits);
+  int32_t* idx = at<int32_t>(saved, sl.idx);
+  float* w = at<float>(saved, sl.w);
+
+  MOE_TRY(launch_quant_rows(x, 0, m.T, m.d, xq, xs, stream));
+  MOE_TRY(launch_router_logits((const uint16_t*)x, (const uint16_t*)w_router, router_bias, logits, (int)m.T, d,
+                               (int)m.E, stream));
+  MOE_TRY(launch_topk(logits, (int)m.T, (int)m.E, (int)m.k, cfg->score_fn, idx, w, stream));
+
+  SchedBuild sb;
+  sb.idx = idx;
+  sb.blkcnt = at<int32_t>(workspace, wl.blkcnt);
+  sb.counts = at<int32_t>(saved, sl.counts);
+  sb.offsets = at<int32_t>(saved, sl.offsets);
+  sb.poffsets = at<int32_t>(saved, sl.poffsets);
+  sb.tok_off = at<int64_t>(saved, sl.tok_off);
+  sb.tile_start = at<int32_t>(saved, sl.tile_start);
+  sb.tile64 = at<int32_t>(saved, sl.tile64);
+  sb.perm = at<int32_t>(saved, sl.perm);
+  sb.pos = at<int32_t>(saved, sl.pos);
+  sb.T = (int)m.T;
+  sb.E = (int)m.E;
+  sb.k = (int)m.k;
+  sb.S = (int)m.S;
+  MOE_TRY(launch_schedule(sb, stream));
+
+  const SchedView sv = sched_view(saved, sl, m);
+  GateUpArgs ga;
+  ga.s = sv;
+  ga.xq = xq;
+  ga.xs = xs;
+  ga.w1q = w1q;
+  ga.w1s = w1s;
+  ga.g = at<float>(saved, sl.g);
+  ga.u = at<float>(saved, sl.u);
+  ga.hq = at<uint8_t>(saved, sl.hq);
+  ga.hs = at<uint8_t>(saved, sl.hs);
+  ga.d = d;
+  ga.I = I;
+  MOE_TRY(launch_gemm_gateup(ga, (int)m.tiles_bound, stream));
+
+  DownArgs da;
+  da.s = sv;
+  da.hq = ga.hq;
+  da.hs = ga.hs;
+  da.w2q = w2q;
+  da.w2s = w2s;
+  da.yslot = at<float>(saved, sl.yslot);
+  da.d = d;
+  da.I = I;
+  MOE_TRY(launch_gemm_down(da, (int)m.tiles_bound, stream));
+
+  MOE_TRY(launch_combine(da.yslot, w, (int)m.T, (int)m.k, (int)m.S, d, (uint16_t*)y_bf16, y_f32, stream));
+  return MOE_OK;
+}
+
+moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const void* w_router, const uint8_t* w1q,
+                   const uint8_t* w1s, const uint8_t* w2q, const uint8_t* w2s, const void* saved, void* dx_bf16,
+                   float* dx_f32, float* dw_router, float* dw1, float* dw2, void* workspace, hipStream_t stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!dy || !x || !w_router || !w1q || !w1s || !w2q || !w2s || !saved || !dx_bf16 || !dw_router || !dw1 || !dw2 ||
+      !workspace)
+    return MOE_EINVAL;
+  if (!aligned(dy, 16) || !aligned(x, 16) || !aligned(w_router, 16) || !aligned(w1q, 16) || !aligned(w2q, 16) ||
+      !aligned(dx_bf16, 16) || (dx_f32 && !aligned(dx_f32, 16)) || !aligned(dw_router, 16) || !aligned(dw1, 16) ||
+      !aligned(dw2, 16) || !aligned(saved, kAlign) || !aligned(workspace, kAlign))
+    return MOE_EALIGN;
+  if ((st = ensure_init()) != MOE_OK) return st;
+  const Dims m = dims(*cfg);
+  const moe_saved_layout sl = saved_layout(m);
+  const Work wl = work_layout(m);
+  const int d = (int)m.d, I = (int)m.I;
+  const SchedView sv = sched_view(saved, sl, m);
+  const float* w = at<float>(saved, sl.w);
+  const int32_t* idx = at<int32_t>(saved, sl.idx);
+  const int64_t* tok_off = at<int64_t>(saved, sl.tok_off);
+  const int32_t* tile64 = at<int32_t>(saved, sl.tile64);
+
+  uint8_t* dyq = at<uint8_t>(workspace, wl.dyq);
+  uint8_t* dys = at<uint8_t>(workspace, wl.dys);
+  float* dwv = at<float>(workspace, wl.dw);
+  float* dl = at<float>(workspace, wl.dl);
+  MOE_TRY(launch_quant_rows(dy, 0, m.T, m.d, dyq, dys, stream));
+  MOE_TRY(launch_router_bwd((const uint16_t*)dy, at<float>(saved, sl.yslot), at<float>(saved, sl.logits), idx, w,
+                            (int)m.T, (int)m.E, (int)m.k, (int)m.S, d, cfg->score_fn, dwv, dl, stream));
+  MOE_TRY(launch_router_wgrad(sv, dl, (const uint16_t*)x, d, (int)m.E, dw_router, stream));
+
+  // requantise the expert weights along their other axis: W1 along 2I, W2 along d
+  uint8_t* w1tq = at<uint8_t>(workspace, wl.w1tq);
+  uint8_t* w1ts = at<uint8_t>(workspace, wl.w1ts);
+  uint8_t* w2tq = at<uint8_t>(workspace, wl.w2tq);
+  uint8_t* w2ts = at<uint8_t>(workspace, wl.w2ts);
+  MOE_TRY(launch_requant_t(w1q, w1s, m.NX, 2 * m.I, m.d, w1tq, w1ts, stream));
+  MOE_TRY(launch_requant_t(w2q, w2s, m.NX, m.d, m.I, w2tq, w2ts, stream));
+
+  DgradDownArgs dd;
+  dd.s = sv;
+  dd.dyq = dyq;
+  dd.dys = dys;
+  dd.w2tq = w2tq;
+  dd.w2ts = w2ts;
+  dd.w = w;
+  dd.g = at<float>(saved, sl.g);
+  dd.u = at<float>(saved, sl.u);
+  dd.dguq = at<uint8_t>(workspace, wl.dguq);
+  dd.dgus = at<uint8_t>(workspace, wl.dgus);
+  dd.d = d;
+  dd.I = I;
+  MOE_TRY(launch_gemm_dgrad_down(dd, (int)m.tiles_bound, stream));
+
+  DgradGateUpArgs dg;
+  dg.s = sv;
+  dg.dguq = dd.dguq;
+  dg.dgus = dd.dgus;
+  dg.w1tq = w1tq;
+  dg.w1ts = w1ts;
+  dg.dxslot = at<float>(workspace, wl.dxslot);
+  dg.d = d;
+  dg.I = I;
+  MOE_TRY(launch_gemm_dgrad_gateup(dg, (int)m.tiles_bound, stream));
+  MOE_TRY(launch_dx_reduce(dg.dxslot, dl, idx, (const uint16_t*)w_router, (int)m.T, (int)m.k, (int)m.S, d,
+                           (uint16_t*)dx_bf16, dx_f32, stream));
+
+  // token-axis requantisation of the weight-gradient operands
+  TokArgs ta;
+  ta.s = sv;
+  ta.w = w;
+  ta.tok_off = tok_off;
+  ta.tile64 = tile64;
+  ta.ld = m.ld_tok;
+  const int tb = (int)m.tile64_bound;
+  ta.q = at<uint8_t>(saved, sl.xq); ta.qs = at<uint8_t>(saved, sl.xs); ta.cols = d; ta.src = TOK_X;
+  ta.out = at<uint8_t>(workspace, wl.xt); ta.outs = at<uint8_t>(workspace, wl.xts);
+  MOE_TRY(launch_token_requant(ta, tb, stream));
+  ta.q = at<uint8_t>(saved, sl.hq); ta.qs = at<uint8_t>(saved, sl.hs); ta.cols = I; ta.src = TOK_H;
+  ta.out = at<uint8_t>(workspace, wl.ht); ta.outs = at<uint8_t>(workspace, wl.hts);
+  MOE_TRY(launch_token_requant(ta, tb, stream));
+  ta.q = dyq; ta.qs = dys; ta.cols = d; ta.src = TOK_DYW;
+  ta.out = at<uint8_t>(workspace, wl.dyt); ta.outs = at<uint8_t>(workspace, wl.dyts);
+  MOE_TRY(launch_token_requant(ta, tb, stream));
+  ta.q = dd.dguq; ta.qs = dd.dgus; ta.cols = 2 * I; ta.src = TOK_DGU;
+  ta.out = at<uint8_t>(workspace, wl.dgut); ta.outs = at<uint8_t>(workspace, wl.dguts);
+  MOE_TRY(launch_token_requant(ta, tb, stream));
+
+  WgradArgs wa;
+  wa.tok_off = tok_off;
+  wa.ld = m.ld_tok;
+  // dW2[e] [d, I] = dYw^T H
+  wa.at = at<uint8_t>(workspace, wl.dyt); wa.ats = at<uint8_t>(workspace, wl.dyts);
+  wa.bt = at<uint8_t>(workspace, wl.ht); wa.bts = at<uint8_t>(workspace, wl.hts);
+  wa.dw = dw2; wa.M = d; wa.N = I;
+  MOE_TRY(launch_gemm_wgrad(wa, (int)m.NX, stream));
+  // dW1[e] [2I, d] = dGU^T X
+  wa.at = at<uint8_t>(workspace, wl.dgut); wa.ats = at<uint8_t>(workspace, wl.dguts);
+  wa.bt = at<uint8_t>(workspace, wl.xt); wa.bts = at<uint8_t>(workspace, wl.xts);
+  wa.dw = dw1; wa.M = 2 * I; wa.N = d;
+  MOE_TRY(launch_gemm_wgrad(wa, (int)m.NX, stream));
+  return MOE_OK;
+}
+
+moe_status moe_device_status(const void* workspace, int32_t* device_code) {
+  if (!workspace || !device_code) return MOE_EINVAL;
+  int32_t code = 0;
+  if (hipMemcpy(&code, workspace, sizeof(code), hipMemcpyDeviceToHost) != hipSuccess) return MOE_ELAUNCH;
+  *device_code = code;
+  return code == 0 ? MOE_OK : MOE_EDEVICE;
+}
+
+const char* moe_strerror(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument (null pointer or unsupported option)";
+    case MOE_ESHAPE: return "unsupported sizes";
+    case MOE_EALIGN: return "misaligned pointer";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_ELAUNCH: return "kernel launch failed";
+    case MOE_EDEVICE: return "device reported an anomaly";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,120 @@
+// Internal kernel launchers and their argument blocks (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Device-side view of the schedule built by the router/schedule kernels.
+struct SchedView {
+  const int32_t* perm;        // [R] slot id t*k + j of each routed permuted row
+  const int32_t* offsets;     // [n_exp + 1] first permuted row of each expert
+  const int32_t* tile_start;  // [n_exp + 1] first 128-row tile of each expert
+  int n_exp;                  // routed + shared experts
+  int R;                      // routed rows T * k (shared rows follow)
+  int T, k, S;
+};
+
+struct GateUpArgs {
+  SchedView s;
+  const uint8_t *xq, *xs, *w1q, *w1s;
+  float *g, *u;
+  uint8_t *hq, *hs;
+  int d, I;
+};
+
+struct DownArgs {
+  SchedView s;
+  const uint8_t *hq, *hs, *w2q, *w2s;
+  float* yslot;
+  int d, I;
+};
+
+struct DgradDownArgs {
+  SchedView s;
+  const uint8_t *dyq, *dys, *w2tq, *w2ts;
+  const float *w, *g, *u;
+  uint8_t *dguq, *dgus;
+  int d, I;
+};
+
+struct DgradGateUpArgs {
+  SchedView s;
+  const uint8_t *dguq, *dgus, *w1tq, *w1ts;
+  float* dxslot;
+  int d, I;
+};
+
+struct WgradArgs {
+  const uint8_t *at, *ats, *bt, *bts;  // [M][ld], [M][ld/32]; [N][ld], [N][ld/32]
+  const int64_t* tok_off;              // [n_exp + 1] padded token offsets (multiples of 128)
+  float* dw;                           // [n_exp][M][N]
+  int64_t ld;
+  int M, N;
+};
+
+size_t gemm_lds_bytes();
+hipError_t gemm_init();
+hipError_t launch_gemm_gateup(const GateUpArgs&, int tiles_bound, hipStream_t);
+hipError_t launch_gemm_down(const DownArgs&, int tiles_bound, hipStream_t);
+hipError_t launch_gemm_dgrad_down(const DgradDownArgs&, int tiles_bound, hipStream_t);
+hipError_t launch_gemm_dgrad_gateup(const DgradGateUpArgs&, int tiles_bound, hipStream_t);
+hipError_t launch_gemm_wgrad(const WgradArgs&, int n_exp, hipStream_t);
+
+// MXFP8 quantisation along the contiguous axis of a [rows, cols] bf16 (src_f32 = 0) or
+// float32 (src_f32 = 1) matrix.
+hipError_t launch_quant_rows(const void* src, int src_f32, int64_t rows, int64_t cols, uint8_t* q,
+                             uint8_t* s, hipStream_t);
+// Batched transposed requantisation: [batch][rows][cols] quantised along cols ->
+// [batch][cols][rows] quantised along rows.
+hipError_t launch_requant_t(const uint8_t* q, const uint8_t* s, int64_t batch, int64_t rows, int64_t cols,
+                            uint8_t* qt, uint8_t* st, hipStream_t);
+
+// Token-axis requantisation of expert rows into token-contiguous operands of the weight
+// gradient GEMMs.
+enum TokSrc { TOK_X = 0, TOK_H = 1, TOK_DGU = 2, TOK_DYW = 3 };
+struct TokArgs {
+  SchedView s;
+  const uint8_t *q, *qs;     // source codes and scales (rows: tokens for X/DYW, permuted rows else)
+  const float* w;            // combine weights [T*k] (TOK_DYW)
+  const int64_t* tok_off;    // [n_exp + 1] padded token offsets
+  const int32_t* tile64;     // [n_exp + 1] first 64-token tile of each expert
+  uint8_t *out, *outs;       // [cols][ld], [cols][ld/32]
+  int64_t ld;
+  int cols;
+  int src;
+};
+hipError_t launch_token_requant(const TokArgs&, int tiles_bound, hipStream_t);
+
+// Router, top-k and schedule.
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_r, const float* bias, float* logits,
+                                int T, int d, int E, hipStream_t);
+hipError_t launch_topk(const float* logits, int T, int E, int k, int score, int32_t* idx, float* w,
+                       hipStream_t);
+struct SchedBuild {
+  const int32_t* idx;   // [T, k]
+  int32_t* blkcnt;      // [nblk, E] scratch
+  int32_t* counts;      // [n_exp]
+  int32_t* offsets;     // [n_exp + 1]
+  int32_t* poffsets;    // [n_exp + 1] padded to 32
+  int64_t* tok_off;     // [n_exp + 1] padded to 128 (weight-gradient operands)
+  int32_t* tile_start;  // [n_exp + 1] 128-row tiles
+  int32_t* tile64;      // [n_exp + 1] 64-token tiles over the 128-padded segments
+  int32_t* perm;        // [R]
+  int32_t* pos;         // [T, k]
+  int T, E, k, S;
+};
+hipError_t launch_schedule(const SchedBuild&, hipStream_t);
+
+// Combine and backward helpers.
+hipError_t launch_combine(const float* yslot, const float* w, int T, int k, int S, int d, uint16_t* y_bf16,
+                          float* y_f32, hipStream_t);
+hipError_t launch_router_bwd(const uint16_t* dy, const float* yslot, const float* logits, const int32_t* idx,
+                             const float* w, int T, int E, int k, int S, int d, int score, float* dw_out,
+                             float* dl_out, hipStream_t);
+hipError_t launch_router_wgrad(const SchedView& s, const float* dl, const uint16_t* x, int d, int E,
+                               float* dw_r, hipStream_t);
+hipError_t launch_dx_reduce(const float* dxslot, const float* dl, const int32_t* idx, const uint16_t* w_r,
+                            int T, int k, int S, int d, uint16_t* dx_bf16, float* dx_f32, hipStream_t);
+
+}  // namespace moe

@@ -1,0 +1,202 @@
+// MXFP8 quantisation kernels: along rows, transposed requantisation of expert weights, and
+// token-axis requantisation of expert rows for the weight-gradient GEMMs.
+//
+// MXFP8 is the OCP Microscaling v1.0 format named by the pages for the whole layer
+// (knowledge card "Mixture-of-Kittens——面向NVL72的开源MoE训练megakernel", 方法/产品要点):
+// blocks of 32 values share an e8m0 exponent floor(log2 amax) - 8; elements are e4m3 with
+// round-to-nearest-even and saturation at 448.  All three kernels stream HBM: loads and stores
+// are 16 bytes per lane and every block is reduced across the lanes that hold it.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+// ----------------------------------------------------------------------------- along rows
+
+// Each lane owns 8 consecutive values; 4 lanes form a 32-value block.
+template <bool F32>
+__global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ src, int64_t n8,
+                                                    uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < n8; g += stride) {
+    float v[8];
+    if (F32) {
+      const v4f* p = (const v4f*)src + 2 * g;
+      v4f a = p[0], b = p[1];
+      v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+      v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+    } else {
+      v4i a = ((const v4i*)src)[g];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t w = (uint32_t)a[j];
+        v[2 * j] = __uint_as_float(w << 16);
+        v[2 * j + 1] = __uint_as_float(w & 0xFFFF0000u);
+      }
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+    m = group_max<4>(m);
+    uint32_t byte = e8m0_from_amax(m);
+    float inv = e8m0_inv_scale(byte);
+    v2i out;
+    out[0] = (int)pack4_e4m3(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    out[1] = (int)pack4_e4m3(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+    ((v2i*)q)[g] = out;
+    if ((g & 3) == 0) s[g >> 2] = (uint8_t)byte;
+  }
+}
+
+// ----------------------------------------------------------------------------- transposed tiles
+//
+// A 64 x 64 float tile is staged in LDS transposed (tile[c][r]); each output row c is then
+// quantised along r in two 32-value blocks.  Lane t handles output row t / 4, values
+// [16 (t % 4), +16); lanes t and t ^ 1 share a block.
+
+constexpr int TS = 64;
+constexpr int TP = TS + 1;  // padded row of the LDS tile (floats)
+
+MOE_DEV void quant_tile_out(const float* tile, uint8_t* out_row, uint8_t* out_scale_row, int part) {
+  const int c = threadIdx.x >> 2;
+  const float* src = tile + c * TP + 16 * part;
+  float v[16];
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    v[j] = src[j];
+    m = fmaxf(m, fabsf(v[j]));
+  }
+  m = fmaxf(m, __shfl_xor(m, 1, 4));
+  uint32_t byte = e8m0_from_amax(m);
+  float inv = e8m0_inv_scale(byte);
+  v4i o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    o[j] = (int)pack4_e4m3(v[4 * j] * inv, v[4 * j + 1] * inv, v[4 * j + 2] * inv, v[4 * j + 3] * inv);
+  *(v4i*)(out_row + 16 * part) = o;
+  if ((part & 1) == 0) out_scale_row[part >> 1] = (uint8_t)byte;
+}
+
+// Dequantise 16 codes that share one scale byte into floats.
+MOE_DEV void dq16(v4i codes, uint32_t sbyte, float* v) {
+  float sc = e8m0_scale(sbyte);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t w = (uint32_t)codes[j];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) v[4 * j + b] = e4m3_to_f32((w >> (8 * b)) & 0xFFu) * sc;
+  }
+}
+
+// [batch][rows][cols] (blocks along cols) -> [batch][cols][rows] (blocks along rows)
+__global__ __launch_bounds__(256) void k_requant_t(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s,
+                                                   int64_t rows, int64_t cols, uint8_t* __restrict__ qt,
+                                                   uint8_t* __restrict__ st) {
+  __shared__ float tile[TS * TP];
+  const int64_t b = blockIdx.z;
+  const int64_t r0 = (int64_t)blockIdx.y * TS, c0 = (int64_t)blockIdx.x * TS;
+  const int t = threadIdx.x;
+  {
+    const int r = t >> 2, part = t & 3;
+    const int64_t row = r0 + r, col = c0 + 16 * part;
+    v4i codes = *(const v4i*)(q + (b * rows + row) * cols + col);
+    uint32_t sb = s[(b * rows + row) * (cols / 32) + col / 32];
+    float v[16];
+    dq16(codes, sb, v);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) tile[(16 * part + j) * TP + r] = v[j];
+  }
+  __syncthreads();
+  const int c = t >> 2, part = t & 3;
+  quant_tile_out(tile, qt + (b * cols + c0 + c) * rows + r0, st + (b * cols + c0 + c) * (rows / 32) + r0 / 32,
+                 part);
+}
+
+MOE_DEV int find_tile(const int32_t* start, int n, int tile) {
+  int lo = 0, hi = n;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (start[mid] <= tile) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Token-axis requantisation: 64 tokens of one expert x 64 columns per workgroup.
+__global__ __launch_bounds__(256) void k_token_requant(TokArgs p) {
+  __shared__ float tile[TS * TP];
+  const SchedView& s = p.s;
+  const int tile_id = blockIdx.y;
+  if (tile_id >= p.tile64[s.n_exp]) return;
+  const int e = find_tile(p.tile64, s.n_exp, tile_id);
+  const int tl = (tile_id - p.tile64[e]) * TS;   // first local token of the tile
+  const int r0 = s.offsets[e];
+  const int cnt = s.offsets[e + 1] - r0;
+  const int c0 = blockIdx.x * TS;
+  const int t = threadIdx.x;
+  {
+    const int x = t >> 2, part = t & 3;
+    const int col = c0 + 16 * part;
+    float v[16];
+    if (tl + x < cnt) {
+      const int r = r0 + tl + x;
+      int64_t srow;
+      if (p.src == TOK_X || p.src == TOK_DYW) {
+        srow = r < s.R ? s.perm[r] / s.k : (r - s.R) % s.T;
+      } else {
+        srow = r;
+      }
+      v4i codes = *(const v4i*)(p.q + srow * p.cols + col);
+      uint32_t sb = p.qs[srow * (p.cols / 32) + col / 32];
+      dq16(codes, sb, v);
+      if (p.src == TOK_DYW) {
+        float wr = r < s.R ? p.w[s.perm[r]] : 1.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] *= wr;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) tile[(16 * part + j) * TP + x] = v[j];
+  }
+  __syncthreads();
+  const int c = t >> 2, part = t & 3;
+  const int64_t o = p.tok_off[e] + tl;
+  quant_tile_out(tile, p.out + (int64_t)(c0 + c) * p.ld + o, p.outs + (int64_t)(c0 + c) * (p.ld / 32) + o / 32,
+                 part);
+}
+
+}  // namespace
+
+hipError_t launch_quant_rows(const void* src, int src_f32, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s,
+                             hipStream_t st) {
+  int64_t n8 = rows * cols / 8;
+  if (n8 == 0) return hipSuccess;
+  int64_t blocks = (n8 + 255) / 256;
+  if (blocks > 256 * 64) blocks = 256 * 64;
+  if (src_f32)
+    hipLaunchKernelGGL(k_quant_rows<true>, dim3((unsigned)blocks), dim3(256), 0, st, src, n8, q, s);
+  else
+    hipLaunchKernelGGL(k_quant_rows<false>, dim3((unsigned)blocks), dim3(256), 0, st, src, n8, q, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_requant_t(const uint8_t* q, const uint8_t* s, int64_t batch, int64_t rows, int64_t cols,
+                            uint8_t* qt, uint8_t* st, hipStream_t stream) {
+  if (batch == 0) return hipSuccess;
+  dim3 grid((unsigned)(cols / TS), (unsigned)(rows / TS), (unsigned)batch);
+  hipLaunchKernelGGL(k_requant_t, grid, dim3(256), 0, stream, q, s, rows, cols, qt, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_token_requant(const TokArgs& a, int tiles_bound, hipStream_t stream) {
+  dim3 grid((unsigned)(a.cols / TS), (unsigned)tiles_bound);
+  hipLaunchKernelGGL(k_token_requant, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

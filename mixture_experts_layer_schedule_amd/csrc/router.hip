@@ -1,0 +1,222 @@
+// Router logits, top-k selection with combine weights, and the device-side schedule.
+//
+// The pages' layer starts by routing every token to a few experts, and its schedule is built
+// on the GPU with no CPU involvement and reused by the backward pass (knowledge card
+// "Mixture-of-Kittens——面向NVL72的开源MoE训练megakernel", 方法/产品要点; commentary "Cursor 开源
+// MoK…", 什么是MoK).  Everything here runs on the caller's stream with no host synchronisation.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+// ----------------------------------------------------------------------------- logits
+//
+// L = x W_r^T on v_mfma_f32_32x32x16_bf16 (lane l = i + 32h holds row i, 8 K values; result
+// layout as for every 32x32 MFMA).  Four MFMA steps cover 64 K values; lane half h takes the
+// 32 consecutive values [32h, 32h + 32) of that span (8 per step), which only reorders the
+// float32 accumulation, identically on every run.  One wave computes 32 tokens x 32 experts.
+
+__global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                                                       const float* __restrict__ bias, float* __restrict__ L, int T,
+                                                       int d, int E) {
+  const int wave = threadIdx.x >> 6, l = lane_id(), i = l & 31, h = l >> 5;
+  const int t0 = blockIdx.x * 64 + (wave >> 1) * 32;
+  const int e0 = blockIdx.y * 64 + (wave & 1) * 32;
+  const int trow = min(t0 + i, T - 1);
+  const int erow = e0 + i;
+  const bool evalid = erow < E;
+  const uint16_t* pa = x + (size_t)trow * d + 32 * h;
+  const uint16_t* pb = wr + (size_t)min(erow, E - 1) * d + 32 * h;
+  v16f acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  for (int k0 = 0; k0 < d; k0 += 64) {
+    v8bf a[4], b[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      a[s] = *(const v8bf*)(pa + k0 + 8 * s);
+      v8bf bb = *(const v8bf*)(pb + k0 + 8 * s);
+      if (!evalid) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bb[j] = (__bf16)0.0f;
+      }
+      b[s] = bb;
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b[s], acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    int t = t0 + 8 * (v >> 2) + 4 * h + (v & 3);
+    int e = e0 + i;
+    if (t < T && e < E) L[(size_t)t * E + e] = acc[v] + (bias ? bias[e] : 0.0f);
+  }
+}
+
+// ----------------------------------------------------------------------------- top-k
+//
+// One wave per token.  Experts are ranked by logit, best first; equal logits go to the lower
+// expert index.  Weights: softmax over the k selected logits, or sigmoid scores normalised by
+// their sum.
+
+constexpr int kMaxPerLane = 8;  // E <= 512
+
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ L, int T, int E, int k, int score,
+                                              int32_t* __restrict__ idx, float* __restrict__ w) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int l = lane_id();
+  float v[kMaxPerLane];
+  const int nper = (E + 63) / 64;
+#pragma unroll
+  for (int q = 0; q < kMaxPerLane; ++q) {
+    int e = l + 64 * q;
+    v[q] = (q < nper && e < E) ? L[(size_t)t * E + e] : -INFINITY;
+  }
+  uint32_t taken = 0;
+  float sel_v[16];
+  int sel_e[16];
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int be = 0x7FFFFFFF;
+#pragma unroll
+    for (int q = 0; q < kMaxPerLane; ++q) {
+      int e = l + 64 * q;
+      bool ok = q < nper && e < E && !((taken >> q) & 1u);
+      if (ok && (v[q] > bv || (v[q] == bv && e < be))) {
+        bv = v[q];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      float ov = __shfl_xor(bv, o);
+      int oe = __shfl_xor(be, o);
+      if (ov > bv || (ov == bv && oe < be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if (be != 0x7FFFFFFF && (be & 63) == l) taken |= 1u << (be >> 6);
+    sel_v[j] = bv;
+    sel_e[j] = be;
+  }
+  float wsum = 0.0f, wj[16];
+  for (int j = 0; j < k; ++j) {
+    float z = score == 0 ? expf(sel_v[j] - sel_v[0]) : 1.0f / (1.0f + expf(-sel_v[j]));
+    wj[j] = z;
+    wsum += z;
+  }
+  for (int j = 0; j < k; ++j) {
+    if (l == j) {
+      idx[(size_t)t * k + j] = sel_e[j];
+      w[(size_t)t * k + j] = wj[j] / wsum;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- schedule
+//
+// Expert-major stable permutation of the T*k routed slots in three passes: per 256-token block
+// counts, a per-expert exclusive scan over blocks plus the expert offsets, and a scatter in which
+// one thread per expert walks its block's tokens in order.  Shared experts own the rows after
+// the routed ones (all T tokens, in order).
+
+constexpr int kBlkTok = 256;
+
+__global__ __launch_bounds__(256) void k_sched_hist(SchedBuild p) {
+  extern __shared__ int32_t cnt[];
+  for (int e = threadIdx.x; e < p.E; e += blockDim.x) cnt[e] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * kBlkTok + threadIdx.x;
+  if (t < p.T)
+    for (int j = 0; j < p.k; ++j) atomicAdd(&cnt[p.idx[(size_t)t * p.k + j]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < p.E; e += blockDim.x) p.blkcnt[(size_t)blockIdx.x * p.E + e] = cnt[e];
+}
+
+__global__ __launch_bounds__(1024) void k_sched_scan(SchedBuild p, int nblk) {
+  const int n_exp = p.E + p.S;
+  for (int e = threadIdx.x; e < p.E; e += blockDim.x) {
+    int run = 0;
+    for (int b = 0; b < nblk; ++b) {
+      int c = p.blkcnt[(size_t)b * p.E + e];
+      p.blkcnt[(size_t)b * p.E + e] = run;
+      run += c;
+    }
+    p.counts[e] = run;
+  }
+  for (int e = p.E + threadIdx.x; e < n_exp; e += blockDim.x) p.counts[e] = p.T;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int off = 0, poff = 0, tile = 0, t64 = 0;
+    int64_t tok = 0;
+    for (int e = 0; e < n_exp; ++e) {
+      p.offsets[e] = off;
+      p.poffsets[e] = poff;
+      p.tok_off[e] = tok;
+      p.tile_start[e] = tile;
+      p.tile64[e] = t64;
+      int c = p.counts[e];
+      off += c;
+      poff += (c + 31) / 32 * 32;
+      int c128 = (c + 127) / 128 * 128;
+      tok += c128;
+      tile += (c + 127) / 128;
+      t64 += c128 / 64;
+    }
+    p.offsets[n_exp] = off;
+    p.poffsets[n_exp] = poff;
+    p.tok_off[n_exp] = tok;
+    p.tile_start[n_exp] = tile;
+    p.tile64[n_exp] = t64;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_sched_scatter(SchedBuild p) {
+  extern __shared__ int32_t sidx[];
+  const int t0 = blockIdx.x * kBlkTok;
+  const int ntok = min(kBlkTok, p.T - t0);
+  for (int q = threadIdx.x; q < ntok * p.k; q += blockDim.x) sidx[q] = p.idx[(size_t)t0 * p.k + q];
+  __syncthreads();
+  for (int e = threadIdx.x; e < p.E; e += blockDim.x) {
+    int row = p.offsets[e] + p.blkcnt[(size_t)blockIdx.x * p.E + e];
+    for (int tl = 0; tl < ntok; ++tl) {
+      for (int j = 0; j < p.k; ++j) {
+        if (sidx[tl * p.k + j] == e) {
+          int sid = (t0 + tl) * p.k + j;
+          p.perm[row] = sid;
+          p.pos[sid] = row;
+          ++row;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_r, const float* bias, float* logits, int T,
+                                int d, int E, hipStream_t st) {
+  dim3 grid((T + 63) / 64, (E + 63) / 64);
+  hipLaunchKernelGGL(k_router_logits, grid, dim3(256), 0, st, x, w_r, bias, logits, T, d, E);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* logits, int T, int E, int k, int score, int32_t* idx, float* w,
+                       hipStream_t st) {
+  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, k, score, idx, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_schedule(const SchedBuild& p, hipStream_t st) {
+  const int nblk = (p.T + kBlkTok - 1) / kBlkTok;
+  hipLaunchKernelGGL(k_sched_hist, dim3(nblk), dim3(256), p.E * sizeof(int32_t), st, p);
+  hipLaunchKernelGGL(k_sched_scan, dim3(1), dim3(1024), 0, st, p, nblk);
+  hipLaunchKernelGGL(k_sched_scatter, dim3(nblk), dim3(256), kBlkTok * p.k * sizeof(int32_t), st, p);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -23,7 +23,7 @@ from __future__ import annotations
 
 import math
 from concurrent.futures import ThreadPoolExecutor
-from dataclasses import dataclass, field, replace
+from dataclasses import dataclass, replace
 
 import numpy as np
 
@@ -48,7 +48,6 @@ class LayerConfig:
     zipf_lam: float = 0.0   # scale of the Zipf bias
     backward: bool = False  # the workload includes the backward pass
     ring_rows: int = 0      # ring capacity the workload asks for (0 = library default)
-    extra: dict = field(default_factory=dict)
 
     @property
     def rows(self) -> int:
