@@ -1,20 +1,25 @@
 """The layer on the GPU against the oracle on the same seeded inputs.
 
 Bit-exact: top-k selection, schedule (counts, offsets, permutation, inverse), quantised x.
-Within tolerance (max |err| <= 1e-2 x RMS of the oracle tensor, on the float32 copies):
-y, dx, dW_router, dW1, dW2; the bf16 outputs equal the float32 copies rounded to nearest even.
-Bitwise identical across runs.
+Gate/up results: within the accumulation model |G_gpu - G| <= EPS * sum|a b|.
+H codes: equal to the oracle's wherever the oracle's code is unique, admissible elsewhere
+(oracle.envelope: a float32 accumulation may legitimately land on the neighbouring code).
+Float outputs (y, Y slots, dx, dW_router, dW1, dW2, on the float32 copies):
+max |err| <= 1e-2 x RMS of the oracle tensor + the oracle's admissible envelope; the bf16
+outputs equal the float32 copies rounded to nearest even.  Bitwise identical across runs.
 """
 import numpy as np
 import pytest
 
 import moe_inputs
 import oracle
+from oracle import envelope
 from helpers import gpu_layer, log, oracle_layer, rel_err, rms, to_np
 
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-2
+EPS = 2.0 ** -15  # accumulation model of the matrix-core GEMMs (checked on G and U)
 
 MID = moe_inputs.LayerConfig("mid", T=512, d=512, E=16, k=4, inter=256, score="softmax", seed=7)
 MID_SIG = moe_inputs.LayerConfig("mid_sig_shared", T=384, d=256, E=24, k=6, inter=384, score="sigmoid", seed=8,
@@ -71,50 +76,83 @@ def _expert_rows(fw, name):
     return np.concatenate(parts, axis=0)
 
 
-def test_gate_up_and_h(pair):
+def _rows(d, fw):
+    return np.concatenate([d[e] for e in sorted(fw.experts)], axis=0)
+
+
+@pytest.fixture(scope="module")
+def env(pair):
     cfg, inp, fw, bw, layer = pair
+    _, ws, ex, _, _ = oracle_layer(cfg, True)
+    fenv = envelope.forward_envelope(fw, ex, EPS)
+    benv = envelope.backward_envelope(fw, bw, fenv, inp.dy, inp.x, inp.w_r, ex, cfg.score)
+    return fenv, benv
+
+
+def _check(name, got, ref, bound):
+    """max |got - ref| <= TOL * RMS(ref) + bound (elementwise); log how much of the envelope was used."""
+    got = np.asarray(got, dtype=np.float64)
+    r = rms(ref)
+    err = np.abs(got - ref)
+    beyond = err > TOL * r
+    log(f"  {name}: max|err|/rms {err.max() / r:.3e}; elements beyond {TOL:g} rms: {int(beyond.sum())} "
+        f"({beyond.mean():.2e}); envelope max {bound.max() / r:.2e} mean {bound.mean() / r:.2e} rms")
+    assert np.all(err <= TOL * r + bound), name
+
+
+def test_gate_up_within_accumulation_model(pair, env):
+    cfg, inp, fw, bw, layer = pair
+    fenv, _ = env
     G = to_np(layer.saved_tensor("g")).astype(np.float64)
     U = to_np(layer.saved_tensor("u")).astype(np.float64)
-    Gr, Ur = _expert_rows(fw, "G"), _expert_rows(fw, "U")
-    eg, eu = rel_err(G, Gr), rel_err(U, Ur)
-    log(f"{cfg.name}: G err/rms {eg:.2e}  U err/rms {eu:.2e}")
-    assert eg < 1e-4 and eu < 1e-4
+    eG, eU = _rows(fenv.eG, fw), _rows(fenv.eU, fw)
+    dG = np.abs(G - _expert_rows(fw, "G"))
+    dU = np.abs(U - _expert_rows(fw, "U"))
+    log(f"{cfg.name}: |G err| / model max {np.max(dG / eG):.3f}, |U err| / model max {np.max(dU / eU):.3f}")
+    assert np.all(dG <= eG) and np.all(dU <= eU)
+
+
+def test_h_codes_admissible(pair, env):
+    cfg, inp, fw, bw, layer = pair
+    fenv, _ = env
     hq = to_np(layer.saved_tensor("hq"))
     hs = to_np(layer.saved_tensor("hs"))
-    Hr = _expert_rows(fw, "Hq")
-    frac = np.mean(hq != Hr)
-    log(f"{cfg.name}: H codes differing from the oracle: {frac:.2e}, scales: {np.mean(hs != _expert_rows(fw, 'Hs')):.2e}")
-    assert frac < 1e-3
+    H = oracle.dequantize(hq, hs, axis=1)
+    lo, hi = _rows(fenv.H_lo, fw), _rows(fenv.H_hi, fw)
+    unique = lo == hi
+    Href = _expert_rows(fw, "H")
+    log(f"{cfg.name}: H ambiguous fraction {1 - unique.mean():.3e}; codes differing {np.mean(H != Href):.3e}")
+    assert np.all(H[unique] == Href[unique])
+    assert np.all((H >= lo) & (H <= hi))
 
 
-def test_forward_output(pair):
+def test_forward_output(pair, env):
     cfg, inp, fw, bw, layer = pair
-    y32 = to_np(layer.y32).astype(np.float64)
-    e = rel_err(y32, fw.y)
-    log(f"{cfg.name}: y max|err|/rms = {e:.3e}")
-    assert e <= TOL
-    assert np.array_equal(to_np(layer.y.view(__import__('torch').int16)), _bf16_rne(to_np(layer.y32)))
-    ys = to_np(layer.saved_tensor("yslot"))
-    assert rel_err(ys[:, : cfg.k].reshape(-1, cfg.d), fw.Yrows[fw.sched.pos.reshape(-1)]) <= TOL
-
-
-def test_backward_outputs(pair):
-    cfg, inp, fw, bw, layer = pair
+    fenv, _ = env
     import torch
-    res = {}
-    res["dx"] = rel_err(to_np(layer.dx32), bw.dx)
-    res["dw_router"] = rel_err(to_np(layer.dw_r), bw.dw_r)
-    dw1 = to_np(layer.dw1)
-    dw2 = to_np(layer.dw2)
+    log(f"{cfg.name}: forward")
+    _check("y", to_np(layer.y32), fw.y, fenv.By)
+    assert np.array_equal(to_np(layer.y.view(torch.int16)), _bf16_rne(to_np(layer.y32)))
+    ys = to_np(layer.saved_tensor("yslot"))
+    _check("Y slots", ys[:, : cfg.k].reshape(-1, cfg.d), fw.Yrows[fw.sched.pos.reshape(-1)],
+           fenv.BY[fw.sched.pos.reshape(-1)])
+
+
+def test_backward_outputs(pair, env):
+    cfg, inp, fw, bw, layer = pair
+    fenv, benv = env
+    import torch
     NX = cfg.E + cfg.n_shared
-    ref1 = np.stack([bw.dW1[e] for e in range(NX)])
-    ref2 = np.stack([bw.dW2[e] for e in range(NX)])
-    res["dW1"] = rel_err(dw1, ref1)
-    res["dW2"] = rel_err(dw2, ref2)
-    log(f"{cfg.name}: backward max|err|/rms " + ", ".join(f"{k} {v:.3e}" for k, v in res.items()))
+    log(f"{cfg.name}: backward")
+    _check("dx", to_np(layer.dx32), bw.dx, benv.Bdx)
+    _check("dW_router", to_np(layer.dw_r), bw.dw_r, benv.Bdw_r)
+    zero = {e: np.zeros_like(bw.dW1[e]) for e in range(NX)}
+    _check("dW1", to_np(layer.dw1), np.stack([bw.dW1[e] for e in range(NX)]),
+           np.stack([benv.BdW1.get(e, zero[e]) for e in range(NX)]))
+    zero2 = {e: np.zeros_like(bw.dW2[e]) for e in range(NX)}
+    _check("dW2", to_np(layer.dw2), np.stack([bw.dW2[e] for e in range(NX)]),
+           np.stack([benv.BdW2.get(e, zero2[e]) for e in range(NX)]))
     assert np.array_equal(to_np(layer.dx.view(torch.int16)), _bf16_rne(to_np(layer.dx32)))
-    for k, v in res.items():
-        assert v <= TOL, k
 
 
 def test_bitwise_reproducible(pair):
