@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Throughput of one DeepSeek-V3-shape MoE layer, forward + backward, on one MI355X.
+
+Workload: T=8192 tokens, d=7168, 256 routed experts, top-8 sigmoid-normalised routing,
+SwiGLU inter 2048, MXFP8 (e4m3 + e8m0 1x32 scales) with float32 accumulation, seed 4;
+synthetic inputs (moe_inputs).  A step is moe_fwd + moe_bwd over one batch with every input
+already resident in HBM.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MXFP8_PEAK = 5.0e15       # dense MXFP8 MFMA, FLOP/s (MI355X published)
+HBM_PEAK = 8.0e12         # HBM3E, B/s (MI355X published)
+METRIC = "MoE layer fwd+bwd TFLOPS & tokens/s at DSV3 shape; % of MXFP8 MFMA peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- algorithmic work
+#
+# Bytes and flops each phase must move / compute (the design doc derives them).  R = T*k routed rows,
+# NX experts; weights are MXFP8 (1 byte + 1/32 scale byte per value); activations as stored.
+
+def phase_work(cfg, tok_pad: int) -> dict:
+    T, d, E, k, I, S = cfg.T, cfg.d, cfg.E, cfg.k, cfg.inter, cfg.n_shared
+    NX, R = E + S, T * cfg.k + S * T
+    q = 1 + 1 / 32  # MXFP8 bytes per value
+    w1 = NX * 2 * I * d * q
+    w2 = NX * d * I * q
+    return {
+        "quant_x": (0.0, T * d * 2 + T * d * q),
+        "router": (2.0 * T * d * E, T * d * 2 + E * d * 2 + T * E * 4),
+        "gateup": (2.0 * R * d * 2 * I, w1 + R * d * q + R * I * (4 + 4 + q)),
+        "down": (2.0 * R * I * d, w2 + R * I * q + R * d * 4),
+        "combine": (0.0, R * d * 4 + T * d * (2 + 4)),
+        "quant_dy": (0.0, T * d * 2 + T * d * q),
+        "router_bwd": (2.0 * T * k * d, T * k * d * 4 + T * d * 2),
+        "requant_w": (0.0, 2 * (w1 + w2)),
+        "dgrad_down": (2.0 * R * d * I, w2 + R * d * q + R * I * 8 + R * 2 * I * q),
+        "dgrad_gateup": (2.0 * R * 2 * I * d, w1 + R * 2 * I * q + R * d * 4),
+        "dx_reduce": (0.0, R * d * 4 + T * d * 6),
+        "token_requant": (0.0, (R * (2 * d + 3 * I) * q) + tok_pad * (2 * d + 3 * I) * q),
+        "wgrad_down": (2.0 * R * d * I, NX * d * I * 4 + tok_pad * (d + I) * q),
+        "wgrad_gateup": (2.0 * R * 2 * I * d, NX * 2 * I * d * 4 + tok_pad * (2 * I + d) * q),
+    }
+
+
+# ----------------------------------------------------------------------------- HIP events
+
+class PhaseEvents:
+    """hipEvent_t array handed to the library for per-phase timing on the launch stream."""
+
+    def __init__(self, n):
+        import torch  # noqa: F401  (loads libamdhip64)
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.n = n
+        self.arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            if self.hip.hipEventCreate(ctypes.byref(self.arr, i * ctypes.sizeof(ctypes.c_void_p))) != 0:
+                raise RuntimeError("hipEventCreate failed")
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+
+    def elapsed(self, a, b) -> float:
+        ms = ctypes.c_float(0)
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.arr[a], self.arr[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(cfg, inp, n_experts: int) -> dict:
+    """The float64 oracle timed on a bounded sample: full router/top-k/schedule/combine work on all
+    tokens, the expert forward+backward (with the transposed weight requantisation) on
+    ``n_experts`` experts, scaled to the whole layer."""
+    import numpy as np
+
+    import moe_inputs
+    import oracle
+    from oracle.layer import _qdq
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    x = inp.x.astype(np.float64)
+    t0 = time.perf_counter()
+    L = oracle.router_logits(x, inp.w_r, inp.bias)
+    idx = oracle.select_topk(L, cfg.k)
+    w = oracle.routing_weights(L, idx, cfg.score)
+    sched = oracle.build_schedule(idx, cfg.E)
+    xq, xs = oracle.quantize(x, axis=1)
+    X = oracle.dequantize(xq, xs, axis=1)
+    dyq, dys = oracle.quantize(inp.dy.astype(np.float64), axis=1)
+    DY = oracle.dequantize(dyq, dys, axis=1)
+    t_dense = time.perf_counter() - t0
+    # expert sample: experts with the median load
+    order = np.argsort(sched.counts)
+    sample = [int(e) for e in order[len(order) // 2: len(order) // 2 + n_experts]]
+    t_exp = 0.0
+    rows = 0
+    for e in sample:
+        w1, w2 = moe_inputs.expert_weights(cfg, e)
+        W1 = _qdq(w1, 1, True)[2]
+        W2 = _qdq(w2, 1, True)[2]       # input preparation (the layer receives quantised weights)
+        toks = sched.perm[sched.offsets[e]:sched.offsets[e + 1]] // cfg.k
+        wrow = w.reshape(-1)[sched.perm[sched.offsets[e]:sched.offsets[e + 1]]]
+        t1 = time.perf_counter()
+        fw = oracle.expert_forward(X[toks], W1, W2)
+        W2t = _qdq(W2, 0, True)[2]
+        W1t = _qdq(W1, 0, True)[2]
+        oracle.expert_backward(fw, X[toks], DY[toks], wrow, W1t, W2t)
+        t_exp += time.perf_counter() - t1
+        rows += len(toks)
+    # combine-side work on the sample's rows, scaled like the experts
+    t_total = t_dense + t_exp * (cfg.T * cfg.k) / max(rows, 1)
+    return {
+        "value": cfg.T / t_total, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+        "sample": (f"float64 NumPy oracle: router, top-k, schedule and x/dy quantisation on all {cfg.T} tokens "
+                   f"({t_dense:.1f} s) + expert forward/backward incl. weight requantisation on {len(sample)} "
+                   f"median-load experts ({rows} rows, {t_exp:.1f} s), scaled by routed rows "
+                   f"{cfg.T * cfg.k}/{rows}; estimated layer time {t_total:.1f} s"),
+    }
+
+
+# ----------------------------------------------------------------------------- main
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="dsv3_fwd_bwd")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-experts", type=int, default=2)
+    ap.add_argument("--dominant", default="auto", help="phase reported in roofline (default: longest)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one MI355X: the layer runs with every expert resident on a single GPU; "
+              "runs on more than one GPU are not part of this build (use --gpus 1).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import moe_inputs
+    import mixture_experts_layer_schedule_amd as moe
+    from mixture_experts_layer_schedule_amd import MoeLayer
+
+    cfg = moe_inputs.CONFIGS[args.config]
+    if not cfg.backward:
+        cfg = cfg.with_(backward=True)
+    t0 = time.time()
+    inp = moe_inputs.layer_inputs(cfg, with_dy=True)
+    layer = MoeLayer.from_config(cfg, with_backward=True)
+    layer.set_inputs(inp.x_bits, inp.w_r_bits, inp.bias, inp.dy_bits)
+    log(f"[bench] inputs on device; drawing and quantising {cfg.E + cfg.n_shared} experts")
+    layer.load_experts(moe_inputs.iter_expert_weights(cfg, threads=min(16, os.cpu_count() or 8)))
+    log(f"[bench] setup {time.time() - t0:.1f} s")
+
+    stream = torch.cuda.current_stream()
+    ev = PhaseEvents(len(moe.PHASES))
+    moe.moe_set_phase_events(ctypes.addressof(ev.arr), ev.n)
+
+    def step():
+        layer.forward(stream)
+        layer.backward(stream)
+
+    for i in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done")
+
+    phase_ms = {p: 0.0 for p in moe.PHASES}
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    total_ms = 0.0
+    for i in range(args.steps):
+        start.record(stream)
+        step()
+        stop.record(stream)
+        stop.synchronize()
+        total_ms += start.elapsed_time(stop)
+        prev = None
+        for p, name in enumerate(moe.PHASES):
+            if name in ("fwd_begin", "bwd_begin"):
+                prev = p
+                continue
+            phase_ms[name] += ev.elapsed(prev, p)
+            prev = p
+    torch.cuda.synchronize()
+    moe.moe_set_phase_events(None, 0)
+    code = moe.moe_device_status(layer.workspace)
+    if code != 0:
+        log(f"[bench] device status {code}")
+        return 1
+    ms = total_ms / args.steps
+    for k in phase_ms:
+        phase_ms[k] /= args.steps
+    log(f"[bench] {args.steps} steps, {ms:.3f} ms/step")
+
+    tok_off = layer.saved_tensor("tok_off").cpu().numpy()
+    work = phase_work(cfg, int(tok_off[-1]))
+    flops_fwd = sum(work[p][0] for p in ("gateup", "down"))
+    flops_gemm = sum(work[p][0] for p in ("gateup", "down", "dgrad_down", "dgrad_gateup", "wgrad_down",
+                                          "wgrad_gateup"))
+    gemm_ms = sum(phase_ms[p] for p in ("gateup", "down", "dgrad_down", "dgrad_gateup", "wgrad_down",
+                                         "wgrad_gateup"))
+    tflops = flops_gemm / (ms * 1e-3) / 1e12
+    phases = {}
+    for p, t in phase_ms.items():
+        if p in work and t > 0:
+            f, b = work[p]
+            phases[p] = {"ms": round(t, 4), "tflops": round(f / (t * 1e-3) / 1e12, 2),
+                         "gbps": round(b / (t * 1e-3) / 1e9, 1),
+                         "mfma_frac": round(f / (t * 1e-3) / MXFP8_PEAK, 4),
+                         "roofline_frac": round(max(f / MXFP8_PEAK, b / HBM_PEAK) / (t * 1e-3), 4)}
+    dom = max((p for p in phases), key=lambda p: phases[p]["ms"]) if args.dominant == "auto" else args.dominant
+    f, b = work[dom]
+    t = phase_ms[dom] * 1e-3
+    if f / MXFP8_PEAK >= b / HBM_PEAK:
+        roof = {"bound": "mfma", "achieved": round(f / t / 1e12, 2), "peak": MXFP8_PEAK / 1e12, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(b / t / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = dom
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU baseline: oracle on a sample of {args.cpu_experts} experts")
+        cpu = cpu_baseline(cfg, inp, args.cpu_experts)
+
+    out = {
+        "metric": METRIC,
+        "value": round(cfg.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8",
+        "data": "synthetic",
+        "config": {"workload": (f"{cfg.name}: DeepSeek-V3-shape MoE layer fwd+bwd, T={cfg.T} d={cfg.d} "
+                                f"E={cfg.E} k={cfg.k} I={cfg.inter} {cfg.score}, seed {cfg.seed}"),
+                   "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "inter": cfg.inter, "score": cfg.score,
+                   "n_shared": cfg.n_shared, "seed": cfg.seed, "parallelism": "single GPU"},
+        "tflops": round(tflops, 2),
+        "mfma_frac_layer": round(flops_gemm / (ms * 1e-3) / MXFP8_PEAK, 4),
+        "mfma_frac_gemms": round(flops_gemm / (gemm_ms * 1e-3) / MXFP8_PEAK, 4),
+        "fwd_tflop": round(flops_fwd / 1e12, 3),
+        "phases": phases,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -142,6 +142,22 @@ moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const v
                    const uint8_t* w1s, const uint8_t* w2q, const uint8_t* w2s, const void* saved, void* dx_bf16,
                    float* dx_f32, float* dw_router, float* dw1, float* dw2, void* workspace, hipStream_t stream);
 
+/* Phase timing, for measurement only.  Phases of moe_fwd / moe_bwd, in launch order; the
+ * library records events[p] on the call's stream right after phase p has been enqueued (and
+ * events[MOE_PH_FWD_BEGIN] / events[MOE_PH_BWD_BEGIN] before the first launch), so the time
+ * of phase p is the elapsed time between the previous recorded event and events[p].  The
+ * caller creates the events (hipEventCreate) and keeps them alive; n_events = 0 turns timing
+ * off.  Results are unaffected. */
+enum {
+  MOE_PH_FWD_BEGIN = 0, MOE_PH_QUANT_X, MOE_PH_ROUTER, MOE_PH_TOPK, MOE_PH_SCHEDULE, MOE_PH_GATEUP,
+  MOE_PH_DOWN, MOE_PH_COMBINE,
+  MOE_PH_BWD_BEGIN, MOE_PH_QUANT_DY, MOE_PH_ROUTER_BWD, MOE_PH_ROUTER_WGRAD, MOE_PH_REQUANT_W,
+  MOE_PH_DGRAD_DOWN, MOE_PH_DGRAD_GATEUP, MOE_PH_DX_REDUCE, MOE_PH_TOKEN_REQUANT, MOE_PH_WGRAD_DOWN,
+  MOE_PH_WGRAD_GATEUP,
+  MOE_PH_COUNT
+};
+moe_status moe_set_phase_events(hipEvent_t* events, int32_t n_events);
+
 /* Reads the device status word of `workspace` (0 = fine) into *device_code.  Blocking copy:
  * call after the caller has synchronised the stream.  Returns MOE_EDEVICE if the code is
  * non-zero. */

@@ -19,7 +19,12 @@ MOE_F_DIRECT_GATHER = 1
 
 # every symbol include/moe.h declares
 EXPORTS = ("moe_query", "moe_quantize_mxfp8", "moe_requant_transpose", "moe_fwd", "moe_bwd",
-           "moe_device_status", "moe_strerror")
+           "moe_set_phase_events", "moe_device_status", "moe_strerror")
+
+# phases of moe_fwd / moe_bwd (include/moe.h, MOE_PH_*)
+PHASES = ("fwd_begin", "quant_x", "router", "topk", "schedule", "gateup", "down", "combine",
+          "bwd_begin", "quant_dy", "router_bwd", "router_wgrad", "requant_w", "dgrad_down", "dgrad_gateup",
+          "dx_reduce", "token_requant", "wgrad_down", "wgrad_gateup")
 
 
 class moe_config(ctypes.Structure):
@@ -58,6 +63,7 @@ def lib() -> ctypes.CDLL:
         L.moe_requant_transpose.argtypes = [P, P, I64, I64, I64, P, P, P]
         L.moe_fwd.argtypes = [ctypes.POINTER(moe_config), P, P, P, P, P, P, P, P, P, P, P, P]
         L.moe_bwd.argtypes = [ctypes.POINTER(moe_config), P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
+        L.moe_set_phase_events.argtypes = [P, I32]
         L.moe_device_status.argtypes = [P, ctypes.POINTER(I32)]
         L.moe_strerror.argtypes = [ctypes.c_int]
         L.moe_strerror.restype = ctypes.c_char_p
@@ -129,6 +135,11 @@ def moe_bwd(cfg, dy, x, w_router, w1q, w1s, w2q, w2s, saved, dx_bf16, dx_f32, dw
     _check(lib().moe_bwd(ctypes.byref(cfg), _ptr(dy), _ptr(x), _ptr(w_router), _ptr(w1q), _ptr(w1s), _ptr(w2q),
                          _ptr(w2s), _ptr(saved), _ptr(dx_bf16), _ptr(dx_f32), _ptr(dw_router), _ptr(dw1), _ptr(dw2),
                          _ptr(workspace), _stream(stream)), "moe_bwd")
+
+
+def moe_set_phase_events(events, n_events: int) -> None:
+    """events: address of a host array of hipEvent_t (or None with n_events = 0)."""
+    _check(lib().moe_set_phase_events(events, int(n_events)), "moe_set_phase_events")
 
 
 def moe_device_status(workspace) -> int:

@@ -116,6 +116,14 @@ T* at(void* base, size_t off) { return (T*)((char*)base + off); }
 template <class T>
 const T* at(const void* base, size_t off) { return (const T*)((const char*)base + off); }
 
+// Optional phase timing (measurement only): events recorded after each phase.
+hipEvent_t* g_events = nullptr;
+int g_n_events = 0;
+
+inline void mark(hipStream_t st, int phase) {
+  if (g_events && phase < g_n_events) hipEventRecord(g_events[phase], st);
+}
+
 std::once_flag g_init_once;
 hipError_t g_init_err = hipSuccess;
 
@@ -193,9 +201,12 @@ moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, c
   int32_t* idx = at<int32_t>(saved, sl.idx);
   float* w = at<float>(saved, sl.w);
 
+  mark(stream, MOE_PH_FWD_BEGIN);
   MOE_TRY(launch_quant_rows(x, 0, m.T, m.d, xq, xs, stream));
+  mark(stream, MOE_PH_QUANT_X);
   MOE_TRY(launch_router_logits((const uint16_t*)x, (const uint16_t*)w_router, router_bias, logits, (int)m.T, d,
                                (int)m.E, stream));
+  mark(stream, MOE_PH_ROUTER);
   MOE_TRY(launch_topk(logits, (int)m.T, (int)m.E, (int)m.k, cfg->score_fn, idx, w, stream));
 
   SchedBuild sb;
@@ -213,7 +224,9 @@ moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, c
   sb.E = (int)m.E;
   sb.k = (int)m.k;
   sb.S = (int)m.S;
+  mark(stream, MOE_PH_TOPK);
   MOE_TRY(launch_schedule(sb, stream));
+  mark(stream, MOE_PH_SCHEDULE);
 
   const SchedView sv = sched_view(saved, sl, m);
   GateUpArgs ga;
@@ -229,6 +242,7 @@ moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, c
   ga.d = d;
   ga.I = I;
   MOE_TRY(launch_gemm_gateup(ga, (int)m.tiles_bound, stream));
+  mark(stream, MOE_PH_GATEUP);
 
   DownArgs da;
   da.s = sv;
@@ -240,8 +254,10 @@ moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, c
   da.d = d;
   da.I = I;
   MOE_TRY(launch_gemm_down(da, (int)m.tiles_bound, stream));
+  mark(stream, MOE_PH_DOWN);
 
   MOE_TRY(launch_combine(da.yslot, w, (int)m.T, (int)m.k, (int)m.S, d, (uint16_t*)y_bf16, y_f32, stream));
+  mark(stream, MOE_PH_COMBINE);
   return MOE_OK;
 }
 
@@ -272,10 +288,14 @@ moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const v
   uint8_t* dys = at<uint8_t>(workspace, wl.dys);
   float* dwv = at<float>(workspace, wl.dw);
   float* dl = at<float>(workspace, wl.dl);
+  mark(stream, MOE_PH_BWD_BEGIN);
   MOE_TRY(launch_quant_rows(dy, 0, m.T, m.d, dyq, dys, stream));
+  mark(stream, MOE_PH_QUANT_DY);
   MOE_TRY(launch_router_bwd((const uint16_t*)dy, at<float>(saved, sl.yslot), at<float>(saved, sl.logits), idx, w,
                             (int)m.T, (int)m.E, (int)m.k, (int)m.S, d, cfg->score_fn, dwv, dl, stream));
+  mark(stream, MOE_PH_ROUTER_BWD);
   MOE_TRY(launch_router_wgrad(sv, dl, (const uint16_t*)x, d, (int)m.E, dw_router, stream));
+  mark(stream, MOE_PH_ROUTER_WGRAD);
 
   // requantise the expert weights along their other axis: W1 along 2I, W2 along d
   uint8_t* w1tq = at<uint8_t>(workspace, wl.w1tq);
@@ -284,6 +304,7 @@ moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const v
   uint8_t* w2ts = at<uint8_t>(workspace, wl.w2ts);
   MOE_TRY(launch_requant_t(w1q, w1s, m.NX, 2 * m.I, m.d, w1tq, w1ts, stream));
   MOE_TRY(launch_requant_t(w2q, w2s, m.NX, m.d, m.I, w2tq, w2ts, stream));
+  mark(stream, MOE_PH_REQUANT_W);
 
   DgradDownArgs dd;
   dd.s = sv;
@@ -299,6 +320,7 @@ moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const v
   dd.d = d;
   dd.I = I;
   MOE_TRY(launch_gemm_dgrad_down(dd, (int)m.tiles_bound, stream));
+  mark(stream, MOE_PH_DGRAD_DOWN);
 
   DgradGateUpArgs dg;
   dg.s = sv;
@@ -310,8 +332,10 @@ moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const v
   dg.d = d;
   dg.I = I;
   MOE_TRY(launch_gemm_dgrad_gateup(dg, (int)m.tiles_bound, stream));
+  mark(stream, MOE_PH_DGRAD_GATEUP);
   MOE_TRY(launch_dx_reduce(dg.dxslot, dl, idx, (const uint16_t*)w_router, (int)m.T, (int)m.k, (int)m.S, d,
                            (uint16_t*)dx_bf16, dx_f32, stream));
+  mark(stream, MOE_PH_DX_REDUCE);
 
   // token-axis requantisation of the weight-gradient operands
   TokArgs ta;
@@ -334,6 +358,7 @@ moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const v
   ta.out = at<uint8_t>(workspace, wl.dgut); ta.outs = at<uint8_t>(workspace, wl.dguts);
   MOE_TRY(launch_token_requant(ta, tb, stream));
 
+  mark(stream, MOE_PH_TOKEN_REQUANT);
   WgradArgs wa;
   wa.tok_off = tok_off;
   wa.ld = m.ld_tok;
@@ -342,11 +367,20 @@ moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const v
   wa.bt = at<uint8_t>(workspace, wl.ht); wa.bts = at<uint8_t>(workspace, wl.hts);
   wa.dw = dw2; wa.M = d; wa.N = I;
   MOE_TRY(launch_gemm_wgrad(wa, (int)m.NX, stream));
+  mark(stream, MOE_PH_WGRAD_DOWN);
   // dW1[e] [2I, d] = dGU^T X
   wa.at = at<uint8_t>(workspace, wl.dgut); wa.ats = at<uint8_t>(workspace, wl.dguts);
   wa.bt = at<uint8_t>(workspace, wl.xt); wa.bts = at<uint8_t>(workspace, wl.xts);
   wa.dw = dw1; wa.M = 2 * I; wa.N = d;
   MOE_TRY(launch_gemm_wgrad(wa, (int)m.NX, stream));
+  mark(stream, MOE_PH_WGRAD_GATEUP);
+  return MOE_OK;
+}
+
+moe_status moe_set_phase_events(hipEvent_t* events, int32_t n_events) {
+  if (n_events < 0 || (n_events > 0 && !events)) return MOE_EINVAL;
+  g_events = n_events ? events : nullptr;
+  g_n_events = n_events;
   return MOE_OK;
 }
 
