@@ -149,6 +149,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-experts", type=int, default=2)
     ap.add_argument("--dominant", default="auto", help="phase reported in roofline (default: longest)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one plain 1 GiB device copy first (scales HBM byte counters)")
+    ap.add_argument("--flags", type=int, default=0, help="moe_config.flags (1 = direct gather)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one MI355X: the layer runs with every expert resident on a single GPU; "
@@ -167,13 +170,21 @@ def main() -> int:
         cfg = cfg.with_(backward=True)
     t0 = time.time()
     inp = moe_inputs.layer_inputs(cfg, with_dy=True)
-    layer = MoeLayer.from_config(cfg, with_backward=True)
+    layer = MoeLayer.from_config(cfg, with_backward=True, flags=args.flags)
     layer.set_inputs(inp.x_bits, inp.w_r_bits, inp.bias, inp.dy_bits)
     log(f"[bench] inputs on device; drawing and quantising {cfg.E + cfg.n_shared} experts")
     layer.load_experts(moe_inputs.iter_expert_weights(cfg, threads=min(16, os.cpu_count() or 8)))
     log(f"[bench] setup {time.time() - t0:.1f} s")
 
     stream = torch.cuda.current_stream()
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("[bench] calibration copy: 1 GiB read + 1 GiB written")
     ev = PhaseEvents(len(moe.PHASES))
     moe.moe_set_phase_events(ctypes.addressof(ev.arr), ev.n)
 

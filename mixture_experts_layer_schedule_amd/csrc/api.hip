@@ -15,7 +15,13 @@ size_t up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Dims {
   int64_t T, d, E, k, I, S, NX, R, RS, nblk, ld_tok, tiles_bound, tile64_bound;
+  int64_t nslots, producers;
 };
+
+constexpr int kChunkRows = 128;      // rows per ring chunk: one GEMM row tile
+constexpr int kDefaultRingRows = 4096;
+constexpr int kDefaultProducers = 16;
+constexpr int kSpinLimit = 1 << 22;  // bounded waits of the ring kernel (~seconds)
 
 Dims dims(const moe_config& c) {
   Dims m;
@@ -27,6 +33,9 @@ Dims dims(const moe_config& c) {
   m.ld_tok = (int64_t)up((size_t)(m.RS + 127 * m.NX), 128);
   m.tiles_bound = m.RS / 128 + m.NX + 1;
   m.tile64_bound = m.ld_tok / 64;
+  const int64_t ring_rows = c.ring_rows ? c.ring_rows : kDefaultRingRows;
+  m.nslots = ring_rows / kChunkRows;
+  m.producers = c.producer_wgs ? c.producer_wgs : kDefaultProducers;
   return m;
 }
 
@@ -36,7 +45,10 @@ moe_status check_config(const moe_config* c) {
   if (c->k < 1 || c->k > 16 || c->E < c->k || c->E > 512) return MOE_ESHAPE;
   if (c->n_shared < 0 || c->n_shared > 1) return MOE_ESHAPE;
   if (c->score_fn != MOE_SCORE_SOFTMAX && c->score_fn != MOE_SCORE_SIGMOID) return MOE_EINVAL;
-  if (c->ring_rows < 0 || c->chunk_rows < 0 || c->producer_wgs < 0) return MOE_ESHAPE;
+  if (c->ring_rows < 0 || c->producer_wgs < 0 || c->producer_wgs > 128) return MOE_ESHAPE;
+  if (c->ring_rows && (c->ring_rows < kChunkRows || c->ring_rows % kChunkRows)) return MOE_ESHAPE;
+  if (c->chunk_rows != 0 && c->chunk_rows != kChunkRows) return MOE_ESHAPE;
+  if (c->flags & ~MOE_F_DIRECT_GATHER) return MOE_EINVAL;
   if ((int64_t)c->T * c->k + (int64_t)c->n_shared * c->T >= (1ll << 30)) return MOE_ESHAPE;
   return MOE_OK;
 }
@@ -77,7 +89,7 @@ moe_saved_layout saved_layout(const Dims& m) {
 }
 
 struct Work {
-  size_t status, blkcnt, dyq, dys, dw, dl, w1tq, w1ts, w2tq, w2ts, dguq, dgus, dxslot;
+  size_t status, ring, ring_s, ring_flags, blkcnt, dyq, dys, dw, dl, w1tq, w1ts, w2tq, w2ts, dguq, dgus, dxslot;
   size_t xt, xts, ht, hts, dyt, dyts, dgut, dguts, total;
 };
 
@@ -85,6 +97,9 @@ Work work_layout(const Dims& m) {
   Work w{};
   Layout L;
   w.status = L.take(64);
+  w.ring = L.take(m.nslots * kChunkRows * m.d);
+  w.ring_s = L.take(m.nslots * kChunkRows * m.d / 32);
+  w.ring_flags = L.take(4 * (2 * m.nslots + 1));
   w.blkcnt = L.take(4 * m.nblk * m.E);
   w.dyq = L.take(m.T * m.d);
   w.dys = L.take(m.T * m.d / 32);
@@ -128,7 +143,10 @@ std::once_flag g_init_once;
 hipError_t g_init_err = hipSuccess;
 
 moe_status ensure_init() {
-  std::call_once(g_init_once, [] { g_init_err = gemm_init(); });
+  std::call_once(g_init_once, [] {
+    g_init_err = gemm_init();
+    if (g_init_err == hipSuccess) g_init_err = ring_init();
+  });
   return g_init_err == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }
 
@@ -241,7 +259,35 @@ moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, c
   ga.hs = at<uint8_t>(saved, sl.hs);
   ga.d = d;
   ga.I = I;
-  MOE_TRY(launch_gemm_gateup(ga, (int)m.tiles_bound, stream));
+  if (cfg->flags & MOE_F_DIRECT_GATHER) {
+    MOE_TRY(launch_gemm_gateup(ga, (int)m.tiles_bound, stream));
+  } else {
+    if (ring_max_resident() <= m.producers) return MOE_ESHAPE;
+    RingArgs ra;
+    ra.s = sv;
+    ra.xq = xq;
+    ra.xs = xs;
+    ra.w1q = w1q;
+    ra.w1s = w1s;
+    ra.g = ga.g;
+    ra.u = ga.u;
+    ra.hq = ga.hq;
+    ra.hs = ga.hs;
+    ra.ring = at<uint8_t>(workspace, wl.ring);
+    ra.ring_s = at<uint8_t>(workspace, wl.ring_s);
+    ra.flags = at<int32_t>(workspace, wl.ring_flags);
+    ra.n_flags = (int)(2 * m.nslots + 1);
+    ra.ready = ra.flags;
+    ra.done = ra.flags + m.nslots;
+    ra.abort_flag = ra.flags + 2 * m.nslots;
+    ra.status = at<int32_t>(workspace, wl.status);
+    ra.d = d;
+    ra.I = I;
+    ra.nslots = (int)m.nslots;
+    ra.producers = (int)m.producers;
+    ra.spin_limit = kSpinLimit;
+    MOE_TRY(launch_ring_gateup(ra, stream));
+  }
   mark(stream, MOE_PH_GATEUP);
 
   DownArgs da;

@@ -53,8 +53,26 @@ struct WgradArgs {
   int M, N;
 };
 
+// Persistent gate/up kernel fed through ring token buffers (producer / consumer workgroups).
+struct RingArgs {
+  SchedView s;
+  const uint8_t *xq, *xs, *w1q, *w1s;
+  float *g, *u;
+  uint8_t *hq, *hs;
+  uint8_t *ring, *ring_s;          // [nslots][128][d], [nslots][128][d/32]
+  int32_t *ready, *done;           // [nslots] each: published lap + 1; finished tiles (cumulative)
+  int32_t* abort_flag;             // set when a bounded wait expires
+  int32_t* status;                 // device status word (sticky)
+  int32_t* flags;                  // ready | done | abort, zeroed before every launch
+  int n_flags;
+  int d, I, nslots, producers, spin_limit;
+};
+
 size_t gemm_lds_bytes();
 hipError_t gemm_init();
+hipError_t ring_init();
+int ring_max_resident();
+hipError_t launch_ring_gateup(const RingArgs&, hipStream_t);
 hipError_t launch_gemm_gateup(const GateUpArgs&, int tiles_bound, hipStream_t);
 hipError_t launch_gemm_down(const DownArgs&, int tiles_bound, hipStream_t);
 hipError_t launch_gemm_dgrad_down(const DgradDownArgs&, int tiles_bound, hipStream_t);

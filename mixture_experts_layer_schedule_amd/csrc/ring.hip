@@ -1,0 +1,160 @@
+// Persistent dispatch + gate/up kernel fed through fixed-capacity ring token buffers.
+//
+// The pages' megakernel splits its SMs between data movement and matrix work, pulls the tokens
+// each expert needs (pull-based dispatch), and stages them in fixed-capacity ring buffers that
+// are reused cyclically, so no CPU sizes buffers per round and no token is dropped (knowledge
+// card "Mixture-of-Kittens——面向NVL72的开源MoE训练megakernel", 方法/产品要点; article "Cursor 為
+// Composer 改造 MoE 訓練…", section "MoK 將運算同通訊塞入同一個核心"; commentary "Cursor 开源
+// MoK…", section 通信压到18微秒).  On one MI355X the same structure is:
+//
+//  * producer workgroups gather the quantised rows of each 128-row chunk (one expert's rows in
+//    schedule order) from xq into a ring slot and publish the slot's lap number;
+//  * consumer workgroups run the MXFP8 gate/up GEMM tiles of each chunk straight out of the ring
+//    slot (same tile code as the direct kernel) and count finished tiles per slot;
+//  * a producer reuses a slot only when every tile of the chunk it held has been counted.
+//
+// Chunks are produced in order and each role walks its work in increasing order, so with every
+// workgroup co-resident (the grid never exceeds the device's resident capacity) the pipeline
+// cannot deadlock.  Every wait is bounded: past `spin_limit` polls the kernel records a status
+// code and all workgroups leave their loops.  Results are bitwise those of the direct kernel.
+#include "common.h"
+#include "gemm_core.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+MOE_DEV bool wait_ge(int32_t* p, int32_t target, int32_t* abort_flag, int32_t* status, int spin_limit) {
+  int it = 0;
+  while (__hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    if (__hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return false;
+    __builtin_amdgcn_s_sleep(2);
+    if (++it > spin_limit) {
+      __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(abort_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+  }
+  return true;
+}
+
+__global__ void k_zero_flags(int32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+__global__ __launch_bounds__(256) void k_ring_gateup(RingArgs p) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ int s_ok;
+  const SchedView& s = p.s;
+  const int n_chunks = s.tile_start[s.n_exp];
+  const int NT = p.I / 64;
+  const int d = p.d, I = p.I;
+  const size_t slot_bytes = (size_t)BM * d;
+  const size_t slot_sbytes = (size_t)BM * (d / 32);
+
+  if ((int)blockIdx.x < p.producers) {
+    // ------------------------------------------------------------------ producer
+    for (int i = blockIdx.x; i < n_chunks; i += p.producers) {
+      const int slot = i % p.nslots, lap = i / p.nslots;
+      if (threadIdx.x == 0) s_ok = lap == 0 || wait_ge(p.done + slot, lap * NT, p.abort_flag, p.status, p.spin_limit);
+      __syncthreads();
+      if (!s_ok) return;
+      const int e = tile_expert(s.tile_start, s.n_exp, i);
+      const int m0 = s.offsets[e] + (i - s.tile_start[e]) * BM;
+      const int rows = min(BM, s.offsets[e + 1] - m0);
+      uint8_t* dst = p.ring + (size_t)slot * slot_bytes;
+      uint8_t* dsts = p.ring_s + (size_t)slot * slot_sbytes;
+      const int c16 = d / 16;
+      for (int c = threadIdx.x; c < rows * c16; c += blockDim.x) {
+        const int row = c / c16, col = c - row * c16;
+        const uint8_t* src = p.xq + (size_t)row_token(s, m0 + row) * d;
+        *(v4i*)(dst + (size_t)row * d + col * 16) = *(const v4i*)(src + col * 16);
+      }
+      const int c4 = d / 128;  // 4-byte words of one row's scales
+      for (int c = threadIdx.x; c < rows * c4; c += blockDim.x) {
+        const int row = c / c4, col = c - row * c4;
+        const uint32_t* src = (const uint32_t*)(p.xs + (size_t)row_token(s, m0 + row) * (d / 32));
+        ((uint32_t*)(dsts + (size_t)row * (d / 32)))[col] = src[col];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __syncthreads();
+      if (threadIdx.x == 0) __hip_atomic_store(p.ready + slot, lap + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
+
+  // -------------------------------------------------------------------- consumer
+  const int cid = blockIdx.x - p.producers;
+  const int n_cons = gridDim.x - p.producers;
+  const int wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+  const int b_row0[2] = {wn * 32, 64 + wn * 32};
+  for (int tau = cid; tau < n_chunks * NT; tau += n_cons) {
+    const int i = tau / NT, nt = tau - i * NT;
+    const int slot = i % p.nslots, lap = i / p.nslots;
+    if (threadIdx.x == 0) s_ok = wait_ge(p.ready + slot, lap + 1, p.abort_flag, p.status, p.spin_limit);
+    __syncthreads();
+    if (!s_ok) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    const int e = tile_expert(s.tile_start, s.n_exp, i);
+    const int m0 = s.offsets[e] + (i - s.tile_start[e]) * BM;
+    const int mend = s.offsets[e + 1];
+    const uint8_t* w1 = p.w1q + (size_t)e * 2 * I * d;
+    const uint8_t* w1s = p.w1s + (size_t)e * 2 * I * (d / 32);
+    const uint8_t* ring = p.ring + (size_t)slot * slot_bytes;
+    const uint8_t* rings = p.ring_s + (size_t)slot * slot_sbytes;
+    const uint8_t* arow[4];
+    const uint8_t* brow[4];
+    for (int q = 0; q < 4; ++q) {
+      const int row = (threadIdx.x >> 3) + 32 * q;
+      arow[q] = ring + (size_t)row * d;
+      const int bi = row < 64 ? nt * 64 + row : I + nt * 64 + (row - 64);
+      brow[q] = w1 + (size_t)bi * d;
+    }
+    const uint8_t* srow;
+    if (threadIdx.x < BM) {
+      srow = rings + (size_t)threadIdx.x * (d / 32);
+    } else {
+      const int row = threadIdx.x - BM;
+      const int bi = row < 64 ? nt * 64 + row : I + nt * 64 + (row - 64);
+      srow = w1s + (size_t)bi * (d / 32);
+    }
+    v16f acc[2][2];
+    mainloop(lds, arow, brow, srow, d, wm * 64, b_row0, acc);
+    gateup_epilogue(acc, m0, mend, nt, wm, wn, I, p.g, p.u, p.hq, p.hs);
+    // every wave has finished reading the slot (the main loop ends on a barrier)
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(p.done + slot, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+struct RingLaunch {
+  int max_resident = 0;
+};
+RingLaunch g_ring;
+
+}  // namespace
+
+hipError_t ring_init() {
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e;
+  if ((e = hipGetDevice(&dev))) return e;
+  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev))) return e;
+  const int bytes = (int)gemm_lds_bytes();
+  if ((e = hipFuncSetAttribute((const void*)k_ring_gateup, hipFuncAttributeMaxDynamicSharedMemorySize, bytes)))
+    return e;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_ring_gateup, 256, bytes))) return e;
+  g_ring.max_resident = cus * per_cu;
+  return hipSuccess;
+}
+
+int ring_max_resident() { return g_ring.max_resident; }
+
+hipError_t launch_ring_gateup(const RingArgs& a, hipStream_t st) {
+  const int grid = g_ring.max_resident;
+  if (grid <= a.producers) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(k_zero_flags, dim3(1), dim3(256), 0, st, a.flags, a.n_flags);
+  hipLaunchKernelGGL(k_ring_gateup, dim3(grid), dim3(256), gemm_lds_bytes(), st, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe
