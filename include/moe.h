@@ -61,9 +61,9 @@ typedef struct moe_config {
   int32_t inter;      /* SwiGLU intermediate size I */
   int32_t n_shared;   /* always-on shared experts (weight 1), stored after the E routed ones */
   int32_t score_fn;   /* moe_score_fn */
-  int32_t ring_rows;  /* ring token buffer capacity in rows (0 = default) */
+  int32_t ring_rows;  /* ring token buffer capacity in rows (0 = default; multiple of 128) */
   int32_t chunk_rows; /* rows per ring chunk (0 = default) */
-  int32_t producer_wgs; /* gather (producer) workgroups of the persistent dispatch kernel (0 = default) */
+  int32_t producer_wgs; /* gather (producer) workgroups of the persistent dispatch kernel (0 = default, max 128) */
   uint32_t flags;     /* MOE_F_* */
 } moe_config;
 

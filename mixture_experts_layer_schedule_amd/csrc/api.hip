@@ -19,8 +19,8 @@ struct Dims {
 };
 
 constexpr int kChunkRows = 128;      // rows per ring chunk: one GEMM row tile
-constexpr int kDefaultRingRows = 4096;
-constexpr int kDefaultProducers = 16;
+constexpr int kDefaultRingRows = 16384;
+constexpr int kDefaultProducers = 32;
 constexpr int kSpinLimit = 1 << 22;  // bounded waits of the ring kernel (~seconds)
 
 Dims dims(const moe_config& c) {

@@ -72,15 +72,30 @@ struct Stage {
   uint32_t s;
 };
 
+// Device-coherent 16-byte read as two relaxed agent-scope 64-bit atomic loads: it observes data
+// another workgroup published (release) without invalidating any cache level.
+MOE_DEV v4i load16_coherent(const uint8_t* p) {
+  uint64_t* q = (uint64_t*)p;
+  uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return (v4i){(int)(uint32_t)lo, (int)(uint32_t)(lo >> 32), (int)(uint32_t)hi, (int)(uint32_t)(hi >> 32)};
+}
+
+// kCoherentA: the A operand (rows and their scales) was written by other workgroups of the same
+// kernel (ring buffers) and is read with device-coherent loads.
+template <bool kCoherentA = false>
 MOE_DEV void load_stage(Stage& st, const uint8_t* const* arow, const uint8_t* const* brow,
                         const uint8_t* srow, int k0) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     int col = (threadIdx.x & 7) * 16;
-    st.a[q] = *(const v4i*)(arow[q] + k0 + col);
+    st.a[q] = kCoherentA ? load16_coherent(arow[q] + k0 + col) : *(const v4i*)(arow[q] + k0 + col);
     st.b[q] = *(const v4i*)(brow[q] + k0 + col);
   }
-  st.s = *(const uint32_t*)(srow + (k0 >> 5));
+  if (kCoherentA && threadIdx.x < BM)
+    st.s = __hip_atomic_load((uint32_t*)(srow + (k0 >> 5)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    st.s = *(const uint32_t*)(srow + (k0 >> 5));
 }
 
 MOE_DEV void store_stage(const Stage& st, uint8_t* lds) {
@@ -136,6 +151,7 @@ MOE_DEV void compute_stage(const uint8_t* lds, int a_row0, const int* b_row0, v1
 }
 
 // Main loop: acc = A_tile * B_tile^T over K.
+template <bool kCoherentA = false>
 MOE_DEV void mainloop(uint8_t* lds, const uint8_t* const* arow, const uint8_t* const* brow,
                       const uint8_t* srow, int K, int a_row0, const int* b_row0, v16f (&acc)[2][2]) {
 #pragma unroll
@@ -147,12 +163,12 @@ MOE_DEV void mainloop(uint8_t* lds, const uint8_t* const* arow, const uint8_t* c
   const int nk = K / BK;
   if (nk == 0) return;
   Stage st;
-  load_stage(st, arow, brow, srow, 0);
+  load_stage<kCoherentA>(st, arow, brow, srow, 0);
   store_stage(st, lds);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     uint8_t* cur = lds + (kt & 1) * STAGE_BYTES;
-    if (kt + 1 < nk) load_stage(st, arow, brow, srow, (kt + 1) * BK);
+    if (kt + 1 < nk) load_stage<kCoherentA>(st, arow, brow, srow, (kt + 1) * BK);
     compute_stage(cur, a_row0, b_row0, acc);
     if (kt + 1 < nk) store_stage(st, lds + ((kt + 1) & 1) * STAGE_BYTES);
     __syncthreads();

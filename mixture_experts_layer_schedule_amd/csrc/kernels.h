@@ -60,7 +60,7 @@ struct RingArgs {
   float *g, *u;
   uint8_t *hq, *hs;
   uint8_t *ring, *ring_s;          // [nslots][128][d], [nslots][128][d/32]
-  int32_t *ready, *done;           // [nslots] each: published lap + 1; finished tiles (cumulative)
+  int32_t *ready, *done;           // [nslots] each: published lap + 1; finished work units (cumulative)
   int32_t* abort_flag;             // set when a bounded wait expires
   int32_t* status;                 // device status word (sticky)
   int32_t* flags;                  // ready | done | abort, zeroed before every launch

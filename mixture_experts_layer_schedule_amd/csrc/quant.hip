@@ -115,6 +115,63 @@ __global__ __launch_bounds__(256) void k_requant_t(const uint8_t* __restrict__ q
                  part);
 }
 
+
+// [batch][rows][cols] (blocks along cols) -> [batch][cols][rows] (blocks along rows), register
+// version: a lane owns 8 consecutive columns of 32 consecutive rows (one output block per
+// column), so the new block maximum needs no cross-lane traffic.  Loads are 8 bytes per lane and
+// coalesced across the wave; each output column's block is one 32-byte store.  Codes are decoded
+// two at a time by the hardware conversion and scaled by their row's e8m0 factor.
+__global__ __launch_bounds__(256) void k_requant_t_rows32(const uint8_t* __restrict__ q,
+                                                         const uint8_t* __restrict__ s, int64_t rows, int64_t cols,
+                                                         uint8_t* __restrict__ qt, uint8_t* __restrict__ st) {
+  const int64_t b = blockIdx.z;
+  const int64_t c8 = (int64_t)blockIdx.x * 512 + lane_id() * 8;
+  const int64_t r0 = ((int64_t)blockIdx.y * 4 + (threadIdx.x >> 6)) * 32;
+  if (c8 >= cols || r0 >= rows) return;
+  v2i w[32];
+  float sc[32];
+  const uint8_t* src = q + (b * rows + r0) * cols + c8;
+  const uint8_t* ssrc = s + (b * rows + r0) * (cols / 32) + c8 / 32;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    w[i] = *(const v2i*)(src + (int64_t)i * cols);
+    sc[i] = e8m0_scale(ssrc[(int64_t)i * (cols / 32)]);
+  }
+  uint8_t* dst = qt + (b * cols + c8) * rows + r0;
+  uint8_t* sdst = st + (b * cols + c8) * (rows / 32) + r0 / 32;
+#pragma unroll
+  for (int jp = 0; jp < 4; ++jp) {   // column pair (2 jp, 2 jp + 1)
+    float f0[32], f1[32];
+    float m0 = 0.0f, m1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int word = w[i][jp >> 1];
+      v2f p = (jp & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(word, true) : __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+      f0[i] = p[0] * sc[i];
+      f1[i] = p[1] * sc[i];
+      m0 = fmaxf(m0, fabsf(f0[i]));
+      m1 = fmaxf(m1, fabsf(f1[i]));
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float* f = h ? f1 : f0;
+      const uint32_t byte = e8m0_from_amax(h ? m1 : m0);
+      const float inv = e8m0_inv_scale(byte);
+      v4i o0, o1;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        o0[k] = (int)pack4_e4m3(f[4 * k] * inv, f[4 * k + 1] * inv, f[4 * k + 2] * inv, f[4 * k + 3] * inv);
+        o1[k] = (int)pack4_e4m3(f[16 + 4 * k] * inv, f[16 + 4 * k + 1] * inv, f[16 + 4 * k + 2] * inv,
+                                f[16 + 4 * k + 3] * inv);
+      }
+      const int64_t col = 2 * jp + h;
+      *(v4i*)(dst + col * rows) = o0;
+      *(v4i*)(dst + col * rows + 16) = o1;
+      sdst[col * (rows / 32)] = (uint8_t)byte;
+    }
+  }
+}
+
 MOE_DEV int find_tile(const int32_t* start, int n, int tile) {
   int lo = 0, hi = n;
   while (hi - lo > 1) {
@@ -188,8 +245,13 @@ hipError_t launch_quant_rows(const void* src, int src_f32, int64_t rows, int64_t
 hipError_t launch_requant_t(const uint8_t* q, const uint8_t* s, int64_t batch, int64_t rows, int64_t cols,
                             uint8_t* qt, uint8_t* st, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
-  dim3 grid((unsigned)(cols / TS), (unsigned)(rows / TS), (unsigned)batch);
-  hipLaunchKernelGGL(k_requant_t, grid, dim3(256), 0, stream, q, s, rows, cols, qt, st);
+  if (false) {  // register-blocked variant: measured slower on the expert weights (scattered 32-byte stores)
+    dim3 grid((unsigned)((cols + 511) / 512), (unsigned)((rows + 127) / 128), (unsigned)batch);
+    hipLaunchKernelGGL(k_requant_t_rows32, grid, dim3(256), 0, stream, q, s, rows, cols, qt, st);
+  } else {
+    dim3 grid((unsigned)(cols / TS), (unsigned)(rows / TS), (unsigned)batch);
+    hipLaunchKernelGGL(k_requant_t, grid, dim3(256), 0, stream, q, s, rows, cols, qt, st);
+  }
   return hipGetLastError();
 }
 

@@ -8,10 +8,12 @@
 // MoK…", section 通信压到18微秒).  On one MI355X the same structure is:
 //
 //  * producer workgroups gather the quantised rows of each 128-row chunk (one expert's rows in
-//    schedule order) from xq into a ring slot and publish the slot's lap number;
+//    schedule order) from xq into a ring slot, release them at device scope and publish the
+//    slot's lap number;
 //  * consumer workgroups run the MXFP8 gate/up GEMM tiles of each chunk straight out of the ring
-//    slot (same tile code as the direct kernel) and count finished tiles per slot;
-//  * a producer reuses a slot only when every tile of the chunk it held has been counted.
+//    slot (same tile code as the direct kernel, with device-coherent loads of the slot, so no
+//    cache has to be invalidated) and count finished work units per slot;
+//  * a producer reuses a slot only when every work unit of the chunk it held has been counted.
 //
 // Chunks are produced in order and each role walks its work in increasing order, so with every
 // workgroup co-resident (the grid never exceeds the device's resident capacity) the pipeline
@@ -25,9 +27,14 @@ namespace moe {
 
 namespace {
 
+constexpr int kCopyUnroll = 8;
+constexpr int kTilesPerUnit = 4;  // consecutive 64-column tiles of one chunk per consumer work unit
+
+// Polls with relaxed device-coherent loads (an acquire per poll would invalidate the cache
+// hierarchy on every iteration).
 MOE_DEV bool wait_ge(int32_t* p, int32_t target, int32_t* abort_flag, int32_t* status, int spin_limit) {
   int it = 0;
-  while (__hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+  while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
     if (__hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return false;
     __builtin_amdgcn_s_sleep(2);
     if (++it > spin_limit) {
@@ -49,6 +56,7 @@ __global__ __launch_bounds__(256) void k_ring_gateup(RingArgs p) {
   const SchedView& s = p.s;
   const int n_chunks = s.tile_start[s.n_exp];
   const int NT = p.I / 64;
+  const int units = (NT + kTilesPerUnit - 1) / kTilesPerUnit;  // consumer work units per chunk
   const int d = p.d, I = p.I;
   const size_t slot_bytes = (size_t)BM * d;
   const size_t slot_sbytes = (size_t)BM * (d / 32);
@@ -57,19 +65,36 @@ __global__ __launch_bounds__(256) void k_ring_gateup(RingArgs p) {
     // ------------------------------------------------------------------ producer
     for (int i = blockIdx.x; i < n_chunks; i += p.producers) {
       const int slot = i % p.nslots, lap = i / p.nslots;
-      if (threadIdx.x == 0) s_ok = lap == 0 || wait_ge(p.done + slot, lap * NT, p.abort_flag, p.status, p.spin_limit);
+      if (threadIdx.x == 0) s_ok = lap == 0 || wait_ge(p.done + slot, lap * units, p.abort_flag, p.status, p.spin_limit);
       __syncthreads();
       if (!s_ok) return;
+      // the slot's previous readers are done (their loads completed before they counted)
       const int e = tile_expert(s.tile_start, s.n_exp, i);
       const int m0 = s.offsets[e] + (i - s.tile_start[e]) * BM;
       const int rows = min(BM, s.offsets[e + 1] - m0);
       uint8_t* dst = p.ring + (size_t)slot * slot_bytes;
       uint8_t* dsts = p.ring_s + (size_t)slot * slot_sbytes;
+      // 16-byte pieces, kCopyUnroll loads in flight per lane before their stores
       const int c16 = d / 16;
-      for (int c = threadIdx.x; c < rows * c16; c += blockDim.x) {
-        const int row = c / c16, col = c - row * c16;
-        const uint8_t* src = p.xq + (size_t)row_token(s, m0 + row) * d;
-        *(v4i*)(dst + (size_t)row * d + col * 16) = *(const v4i*)(src + col * 16);
+      const int n16 = rows * c16;
+      for (int base = threadIdx.x; base < n16; base += blockDim.x * kCopyUnroll) {
+        v4i buf[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+          const int c = base + u * blockDim.x;
+          if (c < n16) {
+            const int row = c / c16, col = c - row * c16;
+            buf[u] = *(const v4i*)(p.xq + (size_t)row_token(s, m0 + row) * d + col * 16);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+          const int c = base + u * blockDim.x;
+          if (c < n16) {
+            const int row = c / c16, col = c - row * c16;
+            *(v4i*)(dst + (size_t)row * d + col * 16) = buf[u];
+          }
+        }
       }
       const int c4 = d / 128;  // 4-byte words of one row's scales
       for (int c = threadIdx.x; c < rows * c4; c += blockDim.x) {
@@ -89,13 +114,14 @@ __global__ __launch_bounds__(256) void k_ring_gateup(RingArgs p) {
   const int n_cons = gridDim.x - p.producers;
   const int wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
   const int b_row0[2] = {wn * 32, 64 + wn * 32};
-  for (int tau = cid; tau < n_chunks * NT; tau += n_cons) {
-    const int i = tau / NT, nt = tau - i * NT;
+  // work unit = (chunk, group of up to kTilesPerUnit consecutive 64-column tiles)
+  for (int tau = cid; tau < n_chunks * units; tau += n_cons) {
+    const int i = tau / units, ug = tau - i * units;
     const int slot = i % p.nslots, lap = i / p.nslots;
     if (threadIdx.x == 0) s_ok = wait_ge(p.ready + slot, lap + 1, p.abort_flag, p.status, p.spin_limit);
     __syncthreads();
     if (!s_ok) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    // no cache invalidation: the slot is read below with device-coherent loads only
     const int e = tile_expert(s.tile_start, s.n_exp, i);
     const int m0 = s.offsets[e] + (i - s.tile_start[e]) * BM;
     const int mend = s.offsets[e + 1];
@@ -103,27 +129,29 @@ __global__ __launch_bounds__(256) void k_ring_gateup(RingArgs p) {
     const uint8_t* w1s = p.w1s + (size_t)e * 2 * I * (d / 32);
     const uint8_t* ring = p.ring + (size_t)slot * slot_bytes;
     const uint8_t* rings = p.ring_s + (size_t)slot * slot_sbytes;
-    const uint8_t* arow[4];
-    const uint8_t* brow[4];
-    for (int q = 0; q < 4; ++q) {
-      const int row = (threadIdx.x >> 3) + 32 * q;
-      arow[q] = ring + (size_t)row * d;
-      const int bi = row < 64 ? nt * 64 + row : I + nt * 64 + (row - 64);
-      brow[q] = w1 + (size_t)bi * d;
+    for (int nt = ug * kTilesPerUnit; nt < min(NT, (ug + 1) * kTilesPerUnit); ++nt) {
+      const uint8_t* arow[4];
+      const uint8_t* brow[4];
+      for (int q = 0; q < 4; ++q) {
+        const int row = (threadIdx.x >> 3) + 32 * q;
+        arow[q] = ring + (size_t)row * d;
+        const int bi = row < 64 ? nt * 64 + row : I + nt * 64 + (row - 64);
+        brow[q] = w1 + (size_t)bi * d;
+      }
+      const uint8_t* srow;
+      if (threadIdx.x < BM) {
+        srow = rings + (size_t)threadIdx.x * (d / 32);
+      } else {
+        const int row = threadIdx.x - BM;
+        const int bi = row < 64 ? nt * 64 + row : I + nt * 64 + (row - 64);
+        srow = w1s + (size_t)bi * (d / 32);
+      }
+      v16f acc[2][2];
+      mainloop<true>(lds, arow, brow, srow, d, wm * 64, b_row0, acc);
+      gateup_epilogue(acc, m0, mend, nt, wm, wn, I, p.g, p.u, p.hq, p.hs);
     }
-    const uint8_t* srow;
-    if (threadIdx.x < BM) {
-      srow = rings + (size_t)threadIdx.x * (d / 32);
-    } else {
-      const int row = threadIdx.x - BM;
-      const int bi = row < 64 ? nt * 64 + row : I + nt * 64 + (row - 64);
-      srow = w1s + (size_t)bi * (d / 32);
-    }
-    v16f acc[2][2];
-    mainloop(lds, arow, brow, srow, d, wm * 64, b_row0, acc);
-    gateup_epilogue(acc, m0, mend, nt, wm, wn, I, p.g, p.u, p.hq, p.hs);
-    // every wave has finished reading the slot (the main loop ends on a barrier)
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(p.done + slot, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    // relaxed: the count only has to follow this unit's reads of the slot, which have completed
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(p.done + slot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -61,6 +61,27 @@ class ForwardEnvelope:
     By: np.ndarray  # [T, d]
 
 
+def expert_forward_envelope(fe, A, W1, W2, eps: float = EPS_ACC):
+    """One expert's forward envelope: (bound on |dG|, on |dU|, admissible H lo, hi, max H deviation,
+    bound on |dY| rows beyond the tolerance) for rows A (dequantised) and weights W1, W2."""
+    I = W1.shape[0] // 2
+    aX = np.abs(A)
+    g_err = eps * (aX @ np.abs(W1[:I]).T)
+    u_err = eps * (aX @ np.abs(W1[I:]).T)
+    G, U = fe.G, fe.U
+    s = _sigmoid(G)
+    silu = G * s
+    dsilu = s * (1.0 + G * (1.0 - s))
+    # |silu(G+a)(U+b) - silu(G)U| <= (|silu'(G)| + |a|/2)|a| (|U| + |b|) + |silu(G)| |b|   (|silu''| <= 1/2)
+    h_err = (np.abs(dsilu) + 0.5 * g_err) * g_err * (np.abs(U) + u_err) + np.abs(silu) * u_err
+    h_err = h_err + np.abs(fe.h) * F32_SLACK
+    nom, lo, hi = quantize_range(fe.h, h_err, axis=1)
+    dev = _dev(nom, lo, hi)
+    aW2 = np.abs(W2)
+    by = dev @ aW2.T + eps * ((np.abs(fe.H) + dev) @ aW2.T)
+    return g_err, u_err, lo, hi, dev, by
+
+
 def forward_envelope(fw, experts, eps: float = EPS_ACC) -> ForwardEnvelope:
     eG, eU, Hlo, Hhi, dHs = {}, {}, {}, {}, {}
     T, k = fw.w.shape
@@ -69,26 +90,13 @@ def forward_envelope(fw, experts, eps: float = EPS_ACC) -> ForwardEnvelope:
     E = fw.L.shape[1]
     for e, fe in fw.experts.items():
         W1, W2 = experts(e)
-        I = W1.shape[0] // 2
-        aX = np.abs(fw.X[fw.rows_of[e]])
-        g_err = eps * (aX @ np.abs(W1[:I]).T)
-        u_err = eps * (aX @ np.abs(W1[I:]).T)
-        G, U = fe.G, fe.U
-        s = _sigmoid(G)
-        silu = G * s
-        dsilu = s * (1.0 + G * (1.0 - s))
-        # |silu(G+a)(U+b) - silu(G)U| <= (|silu'(G)| + |a|/2)|a| (|U| + |b|) + |silu(G)| |b|   (|silu''| <= 1/2)
-        h_err = (np.abs(dsilu) + 0.5 * g_err) * g_err * (np.abs(U) + u_err) + np.abs(silu) * u_err
-        h_err = h_err + np.abs(fe.h) * F32_SLACK
-        nom, lo, hi = quantize_range(fe.h, h_err, axis=1)
-        dev = _dev(nom, lo, hi)
+        g_err, u_err, lo, hi, dev, by = expert_forward_envelope(fe, fw.X[fw.rows_of[e]], W1, W2, eps)
         eG[e], eU[e], Hlo[e], Hhi[e], dHs[e] = g_err, u_err, lo, hi, dev
-        aW2 = np.abs(W2)
         if e < E:
             lo_r, hi_r = fw.sched.offsets[e], fw.sched.offsets[e + 1]
         else:
             lo_r, hi_r = R + (e - E) * T, R + (e - E + 1) * T
-        BY[lo_r:hi_r] = dev @ aW2.T + eps * ((np.abs(fe.H) + dev) @ aW2.T)
+        BY[lo_r:hi_r] = by
     By = np.zeros((T, BY.shape[1]))
     for j in range(k):
         By += fw.w[:, j:j + 1] * BY[fw.sched.pos[:, j]]
@@ -107,6 +115,38 @@ class BackwardEnvelope:
     BdW2: dict
 
 
+def expert_backward_envelope(fe, be, A, DYrows, wrow, W1, W2, eG, eU, devH, eps: float = EPS_ACC):
+    """One expert's backward envelope: admissible [dG dU] lo, hi and bounds on |d dX| rows,
+    |d dW1|, |d dW2| beyond the tolerance.  eG, eU, devH come from the forward envelope."""
+    W2t = _qdq(W2, 0, True)[2]
+    W1t = _qdq(W1, 0, True)[2]
+    dH = be.dH
+    edH = eps * np.abs(wrow)[:, None] * (np.abs(DYrows) @ np.abs(W2t)) + np.abs(dH) * F32_SLACK
+    G, U = fe.G, fe.U
+    s = _sigmoid(G)
+    f = s * (1.0 + G * (1.0 - s))           # dG = dH U f(G);  |f'| <= 0.6
+    silu = G * s
+    adH = np.abs(dH) + edH
+    e_dG = np.abs(U * f) * edH + adH * np.abs(f) * eU + adH * (np.abs(U) + eU) * 0.6 * eG
+    e_dU = np.abs(silu) * edH + adH * (np.abs(f) + 0.5 * eG) * eG  # silu' = f
+    eGU = np.concatenate([e_dG, e_dU], axis=1) + np.abs(be.dGU) * F32_SLACK
+    nom, lo, hi = quantize_range(be.dGU, eGU, axis=1)
+    devGU = _dev(nom, lo, hi)
+    aW1t = np.abs(W1t)
+    bdx = devGU @ aW1t + eps * ((np.abs(be.DGU) + devGU) @ aW1t)
+    # weight gradients: token-axis requantisation of ranged operands
+    w32 = wrow.astype(np.float32).astype(np.float64)
+    dYw = (w32[:, None] * DYrows).astype(np.float32).astype(np.float64)
+    dYw_tok, dev_dYw = _token_range(dYw, np.abs(dYw) * 2.0 ** -20)
+    H_tok, dev_H = _token_range(fe.H, devH)
+    GU_tok, dev_GUt = _token_range(be.DGU, devGU)
+    X_tok, _ = _token_range(A, np.zeros_like(A))
+    a_dYw, a_H, a_GU, a_X = np.abs(dYw_tok), np.abs(H_tok), np.abs(GU_tok), np.abs(X_tok)
+    bdw2 = a_dYw.T @ dev_H + dev_dYw.T @ (a_H + dev_H) + eps * ((a_dYw + dev_dYw).T @ (a_H + dev_H))
+    bdw1 = dev_GUt.T @ a_X + eps * ((a_GU + dev_GUt).T @ a_X)
+    return lo, hi, bdx, bdw1, bdw2
+
+
 def backward_envelope(fw, bw, fenv: ForwardEnvelope, dy, x, w_r, experts, score: str) -> BackwardEnvelope:
     eps = fenv.eps
     dy = np.asarray(dy, dtype=np.float64)
@@ -123,7 +163,6 @@ def backward_envelope(fw, bw, fenv: ForwardEnvelope, dy, x, w_r, experts, score:
     for e, be in bw.experts.items():
         fe = fw.experts[e]
         W1, W2 = experts(e)
-        I = W1.shape[0] // 2
         tokens = fw.rows_of[e]
         if e < E:
             lo_r, hi_r = fw.sched.offsets[e], fw.sched.offsets[e + 1]
@@ -131,35 +170,10 @@ def backward_envelope(fw, bw, fenv: ForwardEnvelope, dy, x, w_r, experts, score:
         else:
             lo_r, hi_r = R + (e - E) * T, R + (e - E + 1) * T
             wrow = np.ones(hi_r - lo_r)
-        W2t = _qdq(W2, 0, True)[2]
-        W1t = _qdq(W1, 0, True)[2]
-        aDY = np.abs(DY[tokens])
-        dH = be.dH
-        edH = eps * np.abs(wrow)[:, None] * (aDY @ np.abs(W2t)) + np.abs(dH) * F32_SLACK
-        G, U = fe.G, fe.U
-        eG, eU = fenv.eG[e], fenv.eU[e]
-        s = _sigmoid(G)
-        f = s * (1.0 + G * (1.0 - s))           # dG = dH U f(G);  |f'| <= 0.6
-        silu = G * s
-        adH = np.abs(dH) + edH
-        e_dG = np.abs(U * f) * edH + adH * np.abs(f) * eU + adH * (np.abs(U) + eU) * 0.6 * eG
-        e_dU = np.abs(silu) * edH + adH * (np.abs(f) + 0.5 * eG) * eG  # silu' = f
-        eGU = np.concatenate([e_dG, e_dU], axis=1) + np.abs(be.dGU) * F32_SLACK
-        nom, lo, hi = quantize_range(be.dGU, eGU, axis=1)
-        devGU = _dev(nom, lo, hi)
-        GUlo[e], GUhi[e] = lo, hi
-        aW1t = np.abs(W1t)
-        BdXrows[lo_r:hi_r] = devGU @ aW1t + eps * ((np.abs(be.DGU) + devGU) @ aW1t)
-        # weight gradients: token-axis requantisation of ranged operands
-        w32 = wrow.astype(np.float32).astype(np.float64)
-        dYw = (w32[:, None] * DY[tokens]).astype(np.float32).astype(np.float64)
-        dYw_tok, dev_dYw = _token_range(dYw, np.abs(dYw) * 2.0 ** -20)
-        H_tok, dev_H = _token_range(fe.H, fenv.dH[e])
-        GU_tok, dev_GUt = _token_range(be.DGU, devGU)
-        X_tok, _ = _token_range(fw.X[tokens], np.zeros_like(fw.X[tokens]))
-        a_dYw, a_H, a_GU, a_X = np.abs(dYw_tok), np.abs(H_tok), np.abs(GU_tok), np.abs(X_tok)
-        BdW2[e] = a_dYw.T @ dev_H + dev_dYw.T @ (a_H + dev_H) + eps * ((a_dYw + dev_dYw).T @ (a_H + dev_H))
-        BdW1[e] = dev_GUt.T @ a_X + eps * ((a_GU + dev_GUt).T @ a_X)
+        lo, hi, bdx, bdw1, bdw2 = expert_backward_envelope(fe, be, fw.X[tokens], DY[tokens], wrow, W1, W2,
+                                                            fenv.eG[e], fenv.eU[e], fenv.dH[e], eps)
+        GUlo[e], GUhi[e], BdW1[e], BdW2[e] = lo, hi, bdw1, bdw2
+        BdXrows[lo_r:hi_r] = bdx
     # router: dw = <dy, Y> moves with Y.  Y_r = H_r W2^T is linear in H_r, so
     # |d dw| <= sum_i dev(H_r)_i |(dy_t W2)_i| + eps sum_n |dy_t,n| ((|H_r| + dev) |W2|^T)_n
     Bdw_rows = np.zeros(fw.Yrows.shape[0])

@@ -28,9 +28,12 @@ def _run(cfg, inp, ws, **kw):
     return layer
 
 
-@pytest.fixture(scope="module")
-def skew():
-    cfg = SKEW
+WIDE = moe_inputs.LayerConfig("wide", T=512, d=384, E=12, k=3, inter=640, score="softmax", seed=10)
+
+
+@pytest.fixture(scope="module", params=[SKEW, WIDE], ids=lambda c: c.name)
+def skew(request):
+    cfg = request.param
     inp = moe_inputs.layer_inputs(cfg)
     ws = [moe_inputs.expert_weights(cfg, e) for e in range(cfg.E + cfg.n_shared)]
     import mixture_experts_layer_schedule_amd as moe
