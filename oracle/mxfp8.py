@@ -48,7 +48,6 @@ def _e4m3_table() -> np.ndarray:
 
 
 E4M3_TABLE = _e4m3_table()
-_POSITIVE = E4M3_TABLE[:127].copy()  # codes 0x00..0x7E, strictly increasing from 0 to 448
 
 
 def e4m3_decode(codes: np.ndarray) -> np.ndarray:
@@ -57,18 +56,26 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
 
 
 def e4m3_encode(v: np.ndarray) -> np.ndarray:
-    """Nearest e4m3 code to each value (ties to the even code); requires |v| <= 448."""
+    """Nearest e4m3 code to each value (ties to the even code); requires |v| <= 448.
+
+    Normal range: |v| = (1 + q/8) * 2^e with e in [-6, 8], so q = rint((|v| / 2^e - 1) * 8)
+    (numpy's rint rounds half to even, and the even q is the even code); q = 8 carries into the
+    next binade.  Below 2^-6 the codes are the multiples q * 2^-9, q = rint(|v| * 2^9), and
+    q = 8 is exactly the smallest normal (code 0x08).
+    """
     v = np.asarray(v, dtype=np.float64)
     mag = np.abs(v)
     if not np.all(mag <= E4M3_MAX):
         raise ValueError("e4m3_encode: value outside [-448, 448]")
-    i = np.clip(np.searchsorted(_POSITIVE, mag, side="left"), 1, 126)
-    lo = _POSITIVE[i - 1]
-    hi = _POSITIVE[i]
-    d_lo = mag - lo
-    d_hi = hi - mag
-    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (i % 2 == 0))
-    code = np.where(take_hi, i, i - 1).astype(np.uint8)
+    mant, ex = np.frexp(mag)           # mag = mant * 2^ex, 0.5 <= mant < 1 (mant = 0 for 0)
+    e = ex - 1                         # mag in [2^e, 2^(e+1))
+    q = np.rint((2.0 * mant - 1.0) * 8.0)
+    carry = q == 8.0
+    e = np.where(carry, e + 1, e)
+    q = np.where(carry, 0.0, q)
+    normal = ((e + 7) << 3).astype(np.int64) + q.astype(np.int64)
+    sub = np.rint(mag * 2.0 ** 9).astype(np.int64)
+    code = np.where(mag < 2.0 ** -6, sub, normal).astype(np.uint8)
     return code | np.where(np.signbit(v), np.uint8(0x80), np.uint8(0))
 
 

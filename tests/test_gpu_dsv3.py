@@ -8,7 +8,7 @@ compute piece by piece on the same seeded inputs:
 * x quantisation, bit-exact;
 * two experts (median and maximum load) end to end: G/U within the accumulation model, H codes
   unique-or-admissible, their Y rows, dW1 and dW2 within 1e-2 RMS + envelope;
-* sampled tokens end to end (all their experts): y and dx within 1e-2 RMS + envelope.
+* a sampled token end to end (all its experts): y and dx within 1e-2 RMS + envelope.
 """
 import numpy as np
 import pytest
@@ -47,6 +47,7 @@ def run():
 
     def experts(e):
         if e not in cache:
+            log(f"dsv3: oracle weights of expert {e}")
             w1, w2 = moe_inputs.expert_weights(cfg, e)
             cache[e] = (_qdq(w1, 1, True)[2], _qdq(w2, 1, True)[2])
         return cache[e]
@@ -139,16 +140,18 @@ def test_sampled_experts_end_to_end(run):
         _check(f"dW2[{e}]", to_np(layer.dw2[e]), be.dW2, bdw2)
 
 
-@pytest.mark.parametrize("t", [0, 4321])
+@pytest.mark.parametrize("t", [4321])
 def test_sampled_token_end_to_end(run, t):
     cfg, inp, layer, experts = run
     x = inp.x[t:t + 1].astype(np.float64)
     dy = inp.dy[t:t + 1].astype(np.float64)
+    log(f"dsv3: token {t}: oracle forward")
     fw = oracle.layer_forward(x, inp.w_r, experts, cfg.k, cfg.score)
+    log(f"dsv3: token {t}, experts {list(fw.idx[0])}: oracle backward")
     bw = oracle.layer_backward(fw, dy, x, inp.w_r, experts, cfg.score)
+    log(f"dsv3: token {t}: envelopes")
     fenv = envelope.forward_envelope(fw, experts, EPS)
     benv = envelope.backward_envelope(fw, bw, fenv, dy, x, inp.w_r, experts, cfg.score)
-    log(f"dsv3: token {t}, experts {list(fw.idx[0])}")
     assert np.array_equal(to_np(layer.saved_tensor("idx")[t]), fw.idx[0])
     _check(f"y[{t}]", to_np(layer.y32[t:t + 1]), fw.y, fenv.By)
     _check(f"dx[{t}]", to_np(layer.dx32[t:t + 1]), bw.dx, benv.Bdx)
