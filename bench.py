@@ -81,6 +81,55 @@ class PhaseEvents:
         return ms.value
 
 
+# ----------------------------------------------------------------------------- HBM traffic
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dsv3_fwd_bwd_hbm_traffic.txt")
+PHASE_DISPATCHES = {  # phase -> kernel dispatches of one step (name#index in launch order)
+    "gateup": ["k_ring_gateup#0"], "down": ["k_gemm_down#0"], "combine": ["k_combine#0"],
+    "router_bwd": ["k_router_bwd#0"], "requant_w": ["k_requant_t#0", "k_requant_t#1"],
+    "dgrad_down": ["k_gemm_dgrad_down#0"], "dgrad_gateup": ["k_gemm_dgrad_gateup#0"],
+    "dx_reduce": ["k_dx_reduce#0"], "wgrad_down": ["k_gemm_wgrad#0"], "wgrad_gateup": ["k_gemm_wgrad#1"],
+}
+
+
+def kernel_sources_hash() -> str:
+    """sha256 (first 16 hex digits) over the HIP sources, to tell whether counters are current."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "mixture_experts_layer_schedule_amd", "csrc", "*"))):
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(phase: str, direct_gather: bool):
+    """HBM bytes (read + written) of one launch of the phase's kernels, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when it is missing or the kernels changed
+    since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read().splitlines()
+    except OSError:
+        return None
+    current = kernel_sources_hash()
+    if not any(line.startswith("# kernel sources sha256[:16]:") and line.split(":")[-1].strip() == current
+               for line in text):
+        return None
+    table = {}
+    for line in text:
+        parts = line.split()
+        if len(parts) == 4 and not line.startswith("#"):
+            table[parts[0]] = float(parts[2]) + float(parts[3])
+    keys = PHASE_DISPATCHES.get(phase)
+    if keys and direct_gather and phase == "gateup":
+        keys = ["k_gemm_gateup#0"]
+    if not keys or any(k not in table for k in keys):
+        return None
+    return round(sum(table[k] for k in keys) * 1e9)
+
+
 # ----------------------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(cfg, inp, n_experts: int) -> dict:
@@ -248,7 +297,7 @@ def main() -> int:
     else:
         roof = {"bound": "hbm", "achieved": round(b / t / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom, bool(args.flags & 1))
     roof["kernel"] = dom
 
     cpu = None

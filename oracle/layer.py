@@ -389,14 +389,15 @@ def layer_backward(fw: LayerForward, dy, x, w_r, experts, score: str, quant: boo
     dXrows = np.zeros_like(fw.Yrows)
     outs, dW1, dW2 = {}, {}, {}
     todo = range(E + fw.n_shared) if expert_subset is None else expert_subset
-    I = None
+    I = next(iter(fw.experts.values())).G.shape[1] if fw.experts else None
     for e in todo:
-        W1, W2 = experts(e)
-        I = W1.shape[0] // 2
         if e not in fw.experts:
+            if I is None:
+                I = experts(e)[0].shape[0] // 2
             dW1[e] = np.zeros((2 * I, d))
             dW2[e] = np.zeros((d, I))
             continue
+        W1, W2 = experts(e)
         tokens = fw.rows_of[e]
         if e < E:
             lo, hi = sched.offsets[e], sched.offsets[e + 1]
