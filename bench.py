@@ -85,7 +85,7 @@ class PhaseEvents:
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dsv3_fwd_bwd_hbm_traffic.txt")
 PHASE_DISPATCHES = {  # phase -> kernel dispatches of one step (name#index in launch order)
-    "gateup": ["k_ring_gateup#0"], "down": ["k_gemm_down#0"], "combine": ["k_combine#0"],
+    "gateup": ["k_gemm_gateup#0"], "down": ["k_gemm_down#0"], "combine": ["k_combine#0"],
     "router_bwd": ["k_router_bwd#0"], "requant_w": ["k_requant_t#0", "k_requant_t#1"],
     "dgrad_down": ["k_gemm_dgrad_down#0"], "dgrad_gateup": ["k_gemm_dgrad_gateup#0"],
     "dx_reduce": ["k_dx_reduce#0"], "wgrad_down": ["k_gemm_wgrad#0"], "wgrad_gateup": ["k_gemm_wgrad#1"],
@@ -104,7 +104,7 @@ def kernel_sources_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(phase: str, direct_gather: bool):
+def measured_traffic(phase: str, ring: bool):
     """HBM bytes (read + written) of one launch of the phase's kernels, from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when it is missing or the kernels changed
     since it was taken."""
@@ -123,8 +123,8 @@ def measured_traffic(phase: str, direct_gather: bool):
         if len(parts) == 4 and not line.startswith("#"):
             table[parts[0]] = float(parts[2]) + float(parts[3])
     keys = PHASE_DISPATCHES.get(phase)
-    if keys and direct_gather and phase == "gateup":
-        keys = ["k_gemm_gateup#0"]
+    if keys and ring and phase == "gateup":
+        keys = ["k_ring_gateup#0"]
     if not keys or any(k not in table for k in keys):
         return None
     return round(sum(table[k] for k in keys) * 1e9)
@@ -200,7 +200,7 @@ def main() -> int:
     ap.add_argument("--dominant", default="auto", help="phase reported in roofline (default: longest)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (scales HBM byte counters)")
-    ap.add_argument("--flags", type=int, default=0, help="moe_config.flags (1 = direct gather)")
+    ap.add_argument("--flags", type=int, default=0, help="moe_config.flags (2 = ring dispatch)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one MI355X: the layer runs with every expert resident on a single GPU; "
@@ -297,7 +297,7 @@ def main() -> int:
     else:
         roof = {"bound": "hbm", "achieved": round(b / t / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(dom, bool(args.flags & 1))
+    roof["traffic"] = measured_traffic(dom, ring=bool(args.flags & 2))
     roof["kernel"] = dom
 
     cpu = None

@@ -61,15 +61,19 @@ typedef struct moe_config {
   int32_t inter;      /* SwiGLU intermediate size I */
   int32_t n_shared;   /* always-on shared experts (weight 1), stored after the E routed ones */
   int32_t score_fn;   /* moe_score_fn */
-  int32_t ring_rows;  /* ring token buffer capacity in rows (0 = default; multiple of 128) */
-  int32_t chunk_rows; /* rows per ring chunk (0 = default) */
+  int32_t ring_rows;  /* ring token buffer capacity in rows (0 = default; multiple of 256) */
+  int32_t chunk_rows; /* rows per ring slot (0 = default; only 256 is supported) */
   int32_t producer_wgs; /* gather (producer) workgroups of the persistent dispatch kernel (0 = default, max 128) */
   uint32_t flags;     /* MOE_F_* */
 } moe_config;
 
-/* MOE_F_DIRECT_GATHER: the forward gate/up GEMM pulls its rows straight from the quantised
- * activations instead of through the ring token buffer (same results; a measurement switch). */
+/* Forward dispatch.  By default the gate/up GEMM pulls its rows straight from the quantised
+ * activations through the schedule (MOE_F_DIRECT_GATHER names that default explicitly).
+ * MOE_F_RING_DISPATCH asks for the persistent producer/consumer kernel fed through the ring
+ * token buffer instead; it is currently rejected with MOE_EINVAL (disabled while a device
+ * memory fault seen with its consumer is investigated).  Both flags together: MOE_EINVAL. */
 #define MOE_F_DIRECT_GATHER 1u
+#define MOE_F_RING_DISPATCH 2u
 
 /* Byte offsets inside the caller-owned `saved` buffer that moe_fwd fills and moe_bwd reads
  * (the schedule is built once and reused by the backward pass).  R = T*k routed rows,
@@ -82,7 +86,7 @@ typedef struct moe_saved_layout {
   size_t offsets;    /* int32 [NX + 1]     first permuted row of each expert */
   size_t poffsets;   /* int32 [NX + 1]     offsets with every count rounded up to 32 */
   size_t tok_off;    /* int64 [NX + 1]     offsets with every count rounded up to 128 */
-  size_t tile_start; /* int32 [NX + 1]     first 128-row tile of each expert */
+  size_t tile_start; /* int32 [NX + 1]     first row tile of each expert (ceil(count / 256) each) */
   size_t tile64;     /* int32 [NX + 1]     first 64-row tile of each 128-padded segment */
   size_t perm;       /* int32 [R]          slot id t*k + j of each routed permuted row */
   size_t pos;        /* int32 [T, k]       permuted row of slot (t, j) */

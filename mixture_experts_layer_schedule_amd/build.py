@@ -11,7 +11,7 @@ LIB = os.path.join(HERE, "libmoe_mi355x.so")
 SOURCES = ["api.hip", "gemm.hip", "quant.hip", "router.hip", "combine.hip", "ring.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",
     # keep the compiler from emitting packed float32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

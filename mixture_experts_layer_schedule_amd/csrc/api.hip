@@ -18,7 +18,7 @@ struct Dims {
   int64_t nslots, producers;
 };
 
-constexpr int kChunkRows = 128;      // rows per ring chunk: one GEMM row tile
+constexpr int kChunkRows = 256;      // rows per ring slot: one GEMM row tile at most
 constexpr int kDefaultRingRows = 16384;
 constexpr int kDefaultProducers = 32;
 constexpr int kSpinLimit = 1 << 22;  // bounded waits of the ring kernel (~seconds)
@@ -31,7 +31,7 @@ Dims dims(const moe_config& c) {
   m.RS = m.R + m.S * m.T;
   m.nblk = (m.T + 255) / 256;
   m.ld_tok = (int64_t)up((size_t)(m.RS + 127 * m.NX), 128);
-  m.tiles_bound = m.RS / 128 + m.NX + 1;
+  m.tiles_bound = m.RS / 256 + m.NX + 1;  // sum over experts of ceil(count / 256)
   m.tile64_bound = m.ld_tok / 64;
   const int64_t ring_rows = c.ring_rows ? c.ring_rows : kDefaultRingRows;
   m.nslots = ring_rows / kChunkRows;
@@ -48,7 +48,9 @@ moe_status check_config(const moe_config* c) {
   if (c->ring_rows < 0 || c->producer_wgs < 0 || c->producer_wgs > 128) return MOE_ESHAPE;
   if (c->ring_rows && (c->ring_rows < kChunkRows || c->ring_rows % kChunkRows)) return MOE_ESHAPE;
   if (c->chunk_rows != 0 && c->chunk_rows != kChunkRows) return MOE_ESHAPE;
-  if (c->flags & ~MOE_F_DIRECT_GATHER) return MOE_EINVAL;
+  if (c->flags & ~(MOE_F_DIRECT_GATHER | MOE_F_RING_DISPATCH)) return MOE_EINVAL;
+  if ((c->flags & MOE_F_DIRECT_GATHER) && (c->flags & MOE_F_RING_DISPATCH)) return MOE_EINVAL;
+  if (c->flags & MOE_F_RING_DISPATCH) return MOE_EINVAL;  // disabled: see the ring kernel's header
   if ((int64_t)c->T * c->k + (int64_t)c->n_shared * c->T >= (1ll << 30)) return MOE_ESHAPE;
   return MOE_OK;
 }
@@ -259,7 +261,7 @@ moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, c
   ga.hs = at<uint8_t>(saved, sl.hs);
   ga.d = d;
   ga.I = I;
-  if (cfg->flags & MOE_F_DIRECT_GATHER) {
+  if (!(cfg->flags & MOE_F_RING_DISPATCH)) {
     MOE_TRY(launch_gemm_gateup(ga, (int)m.tiles_bound, stream));
   } else {
     if (ring_max_resident() <= m.producers) return MOE_ESHAPE;
@@ -411,14 +413,14 @@ moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const v
   // dW2[e] [d, I] = dYw^T H
   wa.at = at<uint8_t>(workspace, wl.dyt); wa.ats = at<uint8_t>(workspace, wl.dyts);
   wa.bt = at<uint8_t>(workspace, wl.ht); wa.bts = at<uint8_t>(workspace, wl.hts);
-  wa.dw = dw2; wa.M = d; wa.N = I;
-  MOE_TRY(launch_gemm_wgrad(wa, (int)m.NX, stream));
+  wa.dw = dw2; wa.M = d; wa.N = I; wa.n_exp = (int)m.NX;
+  MOE_TRY(launch_gemm_wgrad(wa, stream));
   mark(stream, MOE_PH_WGRAD_DOWN);
   // dW1[e] [2I, d] = dGU^T X
   wa.at = at<uint8_t>(workspace, wl.dgut); wa.ats = at<uint8_t>(workspace, wl.dguts);
   wa.bt = at<uint8_t>(workspace, wl.xt); wa.bts = at<uint8_t>(workspace, wl.xts);
-  wa.dw = dw1; wa.M = 2 * I; wa.N = d;
-  MOE_TRY(launch_gemm_wgrad(wa, (int)m.NX, stream));
+  wa.dw = dw1; wa.M = 2 * I; wa.N = d; wa.n_exp = (int)m.NX;
+  MOE_TRY(launch_gemm_wgrad(wa, stream));
   mark(stream, MOE_PH_WGRAD_GATEUP);
   return MOE_OK;
 }

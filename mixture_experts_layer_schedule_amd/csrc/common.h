@@ -1,9 +1,18 @@
 // Shared device helpers of the MoE-layer kernels (gfx950 / CDNA4).
 #pragma once
+#include <utility>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #define MOE_DEV __device__ __forceinline__
+
+// fn.template operator()<I>() for I = 0 .. N-1, expanded at compile time (register arrays
+// indexed by I stay in registers however large the body is).
+template <int N, class Fn>
+MOE_DEV void static_for(Fn&& fn) {
+  [&]<int... I>(std::integer_sequence<int, I...>) { (fn.template operator()<I>(), ...); }(
+      std::make_integer_sequence<int, N>{});
+}
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -80,6 +89,18 @@ MOE_DEV float group_max(float v) {  // max over aligned groups of W lanes (W pow
 #pragma unroll
   for (int o = 1; o < W; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, W));
   return v;
+}
+
+// Maximum over each aligned group of 32 lanes, without the LDS crossbar: row rotations by 8, 4,
+// 2 and 1 (DPP) leave every lane of a 16-lane row with the row maximum, then v_permlane16_swap
+// exchanges the maxima of the two rows of each 32-lane half.
+MOE_DEV float group_max32(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false)));
+  const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return fmaxf(__int_as_float(pr[0]), __int_as_float(pr[1]));
 }
 
 template <int W>

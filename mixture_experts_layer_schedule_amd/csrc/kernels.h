@@ -9,7 +9,7 @@ namespace moe {
 struct SchedView {
   const int32_t* perm;        // [R] slot id t*k + j of each routed permuted row
   const int32_t* offsets;     // [n_exp + 1] first permuted row of each expert
-  const int32_t* tile_start;  // [n_exp + 1] first 128-row tile of each expert
+  const int32_t* tile_start;  // [n_exp + 1] first row tile of each expert (ceil(count / 256) each)
   int n_exp;                  // routed + shared experts
   int R;                      // routed rows T * k (shared rows follow)
   int T, k, S;
@@ -50,7 +50,7 @@ struct WgradArgs {
   const int64_t* tok_off;              // [n_exp + 1] padded token offsets (multiples of 128)
   float* dw;                           // [n_exp][M][N]
   int64_t ld;
-  int M, N;
+  int M, N, n_exp;                     // M a multiple of 128
 };
 
 // Persistent gate/up kernel fed through ring token buffers (producer / consumer workgroups).
@@ -59,7 +59,7 @@ struct RingArgs {
   const uint8_t *xq, *xs, *w1q, *w1s;
   float *g, *u;
   uint8_t *hq, *hs;
-  uint8_t *ring, *ring_s;          // [nslots][128][d], [nslots][128][d/32]
+  uint8_t *ring, *ring_s;          // [nslots][256][d], [nslots][256][d/32]
   int32_t *ready, *done;           // [nslots] each: published lap + 1; finished work units (cumulative)
   int32_t* abort_flag;             // set when a bounded wait expires
   int32_t* status;                 // device status word (sticky)
@@ -77,7 +77,7 @@ hipError_t launch_gemm_gateup(const GateUpArgs&, int tiles_bound, hipStream_t);
 hipError_t launch_gemm_down(const DownArgs&, int tiles_bound, hipStream_t);
 hipError_t launch_gemm_dgrad_down(const DgradDownArgs&, int tiles_bound, hipStream_t);
 hipError_t launch_gemm_dgrad_gateup(const DgradGateUpArgs&, int tiles_bound, hipStream_t);
-hipError_t launch_gemm_wgrad(const WgradArgs&, int n_exp, hipStream_t);
+hipError_t launch_gemm_wgrad(const WgradArgs&, hipStream_t);
 
 // MXFP8 quantisation along the contiguous axis of a [rows, cols] bf16 (src_f32 = 0) or
 // float32 (src_f32 = 1) matrix.
@@ -116,7 +116,7 @@ struct SchedBuild {
   int32_t* offsets;     // [n_exp + 1]
   int32_t* poffsets;    // [n_exp + 1] padded to 32
   int64_t* tok_off;     // [n_exp + 1] padded to 128 (weight-gradient operands)
-  int32_t* tile_start;  // [n_exp + 1] 128-row tiles
+  int32_t* tile_start;  // [n_exp + 1] row tiles of up to 256 rows
   int32_t* tile64;      // [n_exp + 1] 64-token tiles over the 128-padded segments
   int32_t* perm;        // [R]
   int32_t* pos;         // [T, k]

@@ -7,9 +7,9 @@
 // Composer 改造 MoE 訓練…", section "MoK 將運算同通訊塞入同一個核心"; commentary "Cursor 开源
 // MoK…", section 通信压到18微秒).  On one MI355X the same structure is:
 //
-//  * producer workgroups gather the quantised rows of each 128-row chunk (one expert's rows in
-//    schedule order) from xq into a ring slot, release them at device scope and publish the
-//    slot's lap number;
+//  * producer workgroups gather the quantised rows of each chunk (one GEMM row tile: up to 256
+//    of one expert's rows in schedule order) from xq into a ring slot, release them at device
+//    scope and publish the slot's lap number;
 //  * consumer workgroups run the MXFP8 gate/up GEMM tiles of each chunk straight out of the ring
 //    slot (same tile code as the direct kernel, with device-coherent loads of the slot, so no
 //    cache has to be invalidated) and count finished work units per slot;
@@ -19,6 +19,10 @@
 // workgroup co-resident (the grid never exceeds the device's resident capacity) the pipeline
 // cannot deadlock.  Every wait is bounded: past `spin_limit` polls the kernel records a status
 // code and all workgroups leave their loops.  Results are bitwise those of the direct kernel.
+//
+// Status: not launched.  The library rejects MOE_F_RING_DISPATCH: the first device run of this
+// consumer (tile code out of line in consume_tile) ended in a memory fault whose cause has not
+// been identified; a host build of the kernel finds every access in bounds.
 #include "common.h"
 #include "gemm_core.h"
 #include "kernels.h"
@@ -28,7 +32,7 @@ namespace moe {
 namespace {
 
 constexpr int kCopyUnroll = 8;
-constexpr int kTilesPerUnit = 4;  // consecutive 64-column tiles of one chunk per consumer work unit
+constexpr int kTilesPerUnit = 4;  // consecutive 128-column tiles of one chunk per consumer work unit
 
 // Polls with relaxed device-coherent loads (an acquire per poll would invalidate the cache
 // hierarchy on every iteration).
@@ -50,16 +54,51 @@ __global__ void k_zero_flags(int32_t* p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
 }
 
-__global__ __launch_bounds__(256) void k_ring_gateup(RingArgs p) {
+// Consumer tile: rows of one chunk straight out of its ring slot (device-coherent loads, cache
+// policy sc1), 128 I columns of gate and up, SwiGLU + quantisation epilogue.
+template <int F>
+MOE_DEV void ring_tile(const RingArgs& p, uint8_t* lds, const uint8_t* ring, const uint8_t* rings,
+                       const RowTile& rt, int n0) {
+  const int d = p.d, I = p.I;
+  const uint8_t* w1 = p.w1q + (size_t)rt.e * 2 * I * d;
+  const uint8_t* w1s = p.w1s + (size_t)rt.e * 2 * I * (d / 32);
+  const int last = rt.rows - 1;
+  TileLoads<F> L;
+  L.init([&](int r) { return ring + (size_t)min(r, last) * d; },
+         [&](int r) { return w1 + (size_t)gateup_brow(r, n0, I) * d; },
+         [&](int r) { return rings + (size_t)min(r, last) * (d / 32); },
+         [&](int r) { return w1s + (size_t)gateup_brow(r, n0, I) * (d / 32); });
+  v16f acc[F][2];
+  mainloop<F, 4, 16>(lds, L, d / KS, true, acc);
+  gateup_epilogue<F>(acc, rt.r0, rt.rows, n0, I, p.g, p.u, p.hq, p.hs);
+}
+
+// One consumer tile, kept out of line: inlined into the persistent loop, its per-lane address
+// arithmetic for every row-fragment count would be hoisted out of the loop and spilled.
+__device__ __attribute__((noinline)) void consume_tile(const RingArgs& p, uint8_t* lds, const uint8_t* ring,
+                                                       const uint8_t* rings, RowTile rt, int n0) {
+  switch ((rt.rows + 31) >> 5) {
+    case 1: ring_tile<1>(p, lds, ring, rings, rt, n0); break;
+    case 2: ring_tile<2>(p, lds, ring, rings, rt, n0); break;
+    case 3: ring_tile<3>(p, lds, ring, rings, rt, n0); break;
+    case 4: ring_tile<4>(p, lds, ring, rings, rt, n0); break;
+    case 5: ring_tile<5>(p, lds, ring, rings, rt, n0); break;
+    case 6: ring_tile<6>(p, lds, ring, rings, rt, n0); break;
+    case 7: ring_tile<7>(p, lds, ring, rings, rt, n0); break;
+    default: ring_tile<8>(p, lds, ring, rings, rt, n0); break;
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void k_ring_gateup(RingArgs p) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int s_ok;
   const SchedView& s = p.s;
-  const int n_chunks = s.tile_start[s.n_exp];
-  const int NT = p.I / 64;
+  const int n_chunks = s.tile_start[s.n_exp];  // one chunk per row tile
+  const int NT = p.I / 128;
   const int units = (NT + kTilesPerUnit - 1) / kTilesPerUnit;  // consumer work units per chunk
-  const int d = p.d, I = p.I;
-  const size_t slot_bytes = (size_t)BM * d;
-  const size_t slot_sbytes = (size_t)BM * (d / 32);
+  const int d = p.d;
+  const size_t slot_bytes = (size_t)TM * d;
+  const size_t slot_sbytes = (size_t)TM * (d / 32);
 
   if ((int)blockIdx.x < p.producers) {
     // ------------------------------------------------------------------ producer
@@ -69,9 +108,8 @@ __global__ __launch_bounds__(256) void k_ring_gateup(RingArgs p) {
       __syncthreads();
       if (!s_ok) return;
       // the slot's previous readers are done (their loads completed before they counted)
-      const int e = tile_expert(s.tile_start, s.n_exp, i);
-      const int m0 = s.offsets[e] + (i - s.tile_start[e]) * BM;
-      const int rows = min(BM, s.offsets[e + 1] - m0);
+      const RowTile rt = row_tile(s, i);
+      const int rows = max(rt.rows, 0);
       uint8_t* dst = p.ring + (size_t)slot * slot_bytes;
       uint8_t* dsts = p.ring_s + (size_t)slot * slot_sbytes;
       // 16-byte pieces, kCopyUnroll loads in flight per lane before their stores
@@ -84,7 +122,7 @@ __global__ __launch_bounds__(256) void k_ring_gateup(RingArgs p) {
           const int c = base + u * blockDim.x;
           if (c < n16) {
             const int row = c / c16, col = c - row * c16;
-            buf[u] = *(const v4i*)(p.xq + (size_t)row_token(s, m0 + row) * d + col * 16);
+            buf[u] = *(const v4i*)(p.xq + (size_t)row_token(s, rt.r0 + row) * d + col * 16);
           }
         }
 #pragma unroll
@@ -99,7 +137,7 @@ __global__ __launch_bounds__(256) void k_ring_gateup(RingArgs p) {
       const int c4 = d / 128;  // 4-byte words of one row's scales
       for (int c = threadIdx.x; c < rows * c4; c += blockDim.x) {
         const int row = c / c4, col = c - row * c4;
-        const uint32_t* src = (const uint32_t*)(p.xs + (size_t)row_token(s, m0 + row) * (d / 32));
+        const uint32_t* src = (const uint32_t*)(p.xs + (size_t)row_token(s, rt.r0 + row) * (d / 32));
         ((uint32_t*)(dsts + (size_t)row * (d / 32)))[col] = src[col];
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
@@ -112,43 +150,23 @@ __global__ __launch_bounds__(256) void k_ring_gateup(RingArgs p) {
   // -------------------------------------------------------------------- consumer
   const int cid = blockIdx.x - p.producers;
   const int n_cons = gridDim.x - p.producers;
-  const int wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
-  const int b_row0[2] = {wn * 32, 64 + wn * 32};
-  // work unit = (chunk, group of up to kTilesPerUnit consecutive 64-column tiles)
+  // work unit = (chunk, group of up to kTilesPerUnit consecutive 128-column tiles)
   for (int tau = cid; tau < n_chunks * units; tau += n_cons) {
     const int i = tau / units, ug = tau - i * units;
     const int slot = i % p.nslots, lap = i / p.nslots;
+    __syncthreads();  // every wave is done with the LDS buffers and s_ok of the previous unit
     if (threadIdx.x == 0) s_ok = wait_ge(p.ready + slot, lap + 1, p.abort_flag, p.status, p.spin_limit);
     __syncthreads();
     if (!s_ok) return;
     // no cache invalidation: the slot is read below with device-coherent loads only
-    const int e = tile_expert(s.tile_start, s.n_exp, i);
-    const int m0 = s.offsets[e] + (i - s.tile_start[e]) * BM;
-    const int mend = s.offsets[e + 1];
-    const uint8_t* w1 = p.w1q + (size_t)e * 2 * I * d;
-    const uint8_t* w1s = p.w1s + (size_t)e * 2 * I * (d / 32);
+    const RowTile rt = row_tile(s, i);
     const uint8_t* ring = p.ring + (size_t)slot * slot_bytes;
     const uint8_t* rings = p.ring_s + (size_t)slot * slot_sbytes;
-    for (int nt = ug * kTilesPerUnit; nt < min(NT, (ug + 1) * kTilesPerUnit); ++nt) {
-      const uint8_t* arow[4];
-      const uint8_t* brow[4];
-      for (int q = 0; q < 4; ++q) {
-        const int row = (threadIdx.x >> 3) + 32 * q;
-        arow[q] = ring + (size_t)row * d;
-        const int bi = row < 64 ? nt * 64 + row : I + nt * 64 + (row - 64);
-        brow[q] = w1 + (size_t)bi * d;
+    if (rt.rows > 0) {
+      for (int nt = ug * kTilesPerUnit; nt < min(NT, (ug + 1) * kTilesPerUnit); ++nt) {
+        if (nt > ug * kTilesPerUnit) __syncthreads();  // previous tile's LDS reads are done
+        consume_tile(p, lds, ring, rings, rt, nt * 128);
       }
-      const uint8_t* srow;
-      if (threadIdx.x < BM) {
-        srow = rings + (size_t)threadIdx.x * (d / 32);
-      } else {
-        const int row = threadIdx.x - BM;
-        const int bi = row < 64 ? nt * 64 + row : I + nt * 64 + (row - 64);
-        srow = w1s + (size_t)bi * (d / 32);
-      }
-      v16f acc[2][2];
-      mainloop<true>(lds, arow, brow, srow, d, wm * 64, b_row0, acc);
-      gateup_epilogue(acc, m0, mend, nt, wm, wn, I, p.g, p.u, p.hq, p.hs);
     }
     // relaxed: the count only has to follow this unit's reads of the slot, which have completed
     if (threadIdx.x == 0) __hip_atomic_fetch_add(p.done + slot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

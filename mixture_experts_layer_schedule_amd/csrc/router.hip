@@ -164,7 +164,7 @@ __global__ __launch_bounds__(1024) void k_sched_scan(SchedBuild p, int nblk) {
       poff += (c + 31) / 32 * 32;
       int c128 = (c + 127) / 128 * 128;
       tok += c128;
-      tile += (c + 127) / 128;
+      tile += (c + 255) / 256;
       t64 += c128 / 64;
     }
     p.offsets[n_exp] = off;

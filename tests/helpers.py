@@ -37,10 +37,13 @@ def gpu_layer(cfg: moe_inputs.LayerConfig, backward: bool, inp=None, ws=None, **
         layer.load_experts(moe_inputs.iter_expert_weights(cfg))
     else:
         layer.load_experts((e, w1, w2) for e, (w1, w2) in enumerate(ws))
+    log(f"  {cfg.name}: forward")
     layer.forward()
-    if backward:
-        layer.backward()
     torch.cuda.synchronize()
+    if backward:
+        log(f"  {cfg.name}: backward")
+        layer.backward()
+        torch.cuda.synchronize()
     return layer
 
 

@@ -1,5 +1,5 @@
 """Ring token buffers: the persistent producer/consumer gate/up kernel gives bitwise the same
-results as the direct-gather kernel, at every ring capacity (down to one 128-row slot, far below
+results as the direct-gather kernel, at every ring capacity (down to one 256-row slot, far below
 the hottest expert's load) and producer count; no token is dropped.
 """
 import numpy as np
@@ -8,7 +8,10 @@ import pytest
 import moe_inputs
 from helpers import log, to_np
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.skip(
+    reason="ring dispatch disabled: the first run of its consumer on the 256-row tile core ended in a device "
+           "memory fault whose cause is not identified (host emulation finds every access in bounds); "
+           "the library rejects MOE_F_RING_DISPATCH until then")]
 
 SKEW = moe_inputs.LayerConfig("skew", T=1024, d=256, E=32, k=4, inter=256, score="sigmoid", seed=9,
                               n_shared=1, zipf_s=1.1, zipf_lam=1.5)
@@ -28,6 +31,7 @@ def _run(cfg, inp, ws, **kw):
     return layer
 
 
+RING = 2  # MOE_F_RING_DISPATCH
 WIDE = moe_inputs.LayerConfig("wide", T=512, d=384, E=12, k=3, inter=640, score="softmax", seed=10)
 
 
@@ -43,11 +47,11 @@ def skew(request):
     return cfg, inp, ws, ref
 
 
-@pytest.mark.parametrize("ring_rows,producers", [(128, 1), (256, 3), (512, 16), (1024, 8), (8192, 32)])
+@pytest.mark.parametrize("ring_rows,producers", [(256, 1), (512, 3), (768, 16), (1024, 8), (8192, 32)])
 def test_ring_matches_direct_gather(skew, ring_rows, producers):
     cfg, inp, ws, ref = skew
     counts = to_np(ref.saved_tensor("counts"))
-    layer = _run(cfg, inp, ws, ring_rows=ring_rows, producer_wgs=producers)
+    layer = _run(cfg, inp, ws, ring_rows=ring_rows, producer_wgs=producers, flags=RING)
     if ring_rows < counts.max():
         log(f"ring {ring_rows} rows < peak load {counts.max()}: wraps")
     for name in ("g", "u", "hq", "hs", "yslot"):
@@ -58,7 +62,7 @@ def test_ring_matches_direct_gather(skew, ring_rows, producers):
 def test_every_row_processed(skew):
     """Each permuted row got a gate/up result (no row dropped): G rows are all written."""
     cfg, inp, ws, ref = skew
-    layer = _run(cfg, inp, ws, ring_rows=128, producer_wgs=2)
+    layer = _run(cfg, inp, ws, ring_rows=256, producer_wgs=2, flags=RING)
     g = layer.saved_tensor("g")
     g.zero_()
     layer.forward()

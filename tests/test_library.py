@@ -46,6 +46,11 @@ def test_query_layout_is_aligned_and_ordered():
     (dict(n_shared=2), moe.MOE_ESHAPE),
     (dict(score_fn=7), moe.MOE_EINVAL),
     (dict(T=0), moe.MOE_ESHAPE),
+    (dict(ring_rows=128), moe.MOE_ESHAPE),   # ring slots hold 256 rows
+    (dict(chunk_rows=128), moe.MOE_ESHAPE),
+    (dict(producer_wgs=129), moe.MOE_ESHAPE),
+    (dict(flags=3), moe.MOE_EINVAL),         # direct gather and ring dispatch together
+    (dict(flags=8), moe.MOE_EINVAL),         # unknown flag
 ])
 def test_query_rejects_bad_config(kw, status):
     base = dict(T=256, d=256, E=8, k=2, inter=128)
