@@ -24,7 +24,16 @@ MOE_DEV void dispatch_rows(int rows, Body&& body) {
   }
 }
 
-constexpr int kStages = 4;  // routed GEMMs: three K slices in flight
+constexpr int kStages = 2;  // one K slice in flight while the other is multiplied
+
+// Slot (t * (k + S) + j) of every row of a tile, computed once per row into LDS (buf: a stage
+// buffer no wave reads any more) instead of once per lane and row in the epilogue.
+MOE_DEV const int64_t* row_slot_table(const SchedView& s, const RowTile& rt, uint8_t* buf) {
+  int64_t* tbl = (int64_t*)buf;
+  if ((int)threadIdx.x < rt.rows) tbl[threadIdx.x] = row_slot(s, rt.r0 + threadIdx.x);
+  __syncthreads();
+  return tbl;
+}
 
 }  // namespace
 
@@ -39,20 +48,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_gateup(GateUpArgs p) {
   const int I = p.I, d = p.d, NT = I / 128;
   int item;
   if (!xcd_item(s.tile_start[s.n_exp] * NT, &item)) return;
-  const RowTile rt = row_tile(s, item / NT);
+  int nt;
+  const RowTile rt = item_tile(s, item, NT, &nt);
   if (rt.rows <= 0) return;
-  const int n0 = (item % NT) * 128;
+  const int n0 = nt * 128;
   const uint8_t* w1 = p.w1q + (size_t)rt.e * 2 * I * d;
   const uint8_t* w1s = p.w1s + (size_t)rt.e * 2 * I * (d / 32);
   const int last = rt.rows - 1;
   dispatch_rows(rt.rows, [&]<int F>() {
     TileLoads<F> L;
-    L.init([&](int r) { return p.xq + (size_t)row_token(s, rt.r0 + min(r, last)) * d; },
-           [&](int r) { return w1 + (size_t)gateup_brow(r, n0, I) * d; },
-           [&](int r) { return p.xs + (size_t)row_token(s, rt.r0 + min(r, last)) * (d / 32); },
-           [&](int r) { return w1s + (size_t)gateup_brow(r, n0, I) * (d / 32); });
+    L.init(p.xq, [&](int r) { return p.xq + (size_t)row_token(s, rt.r0 + min(r, last)) * d; },
+           w1, [&](int r) { return w1 + (size_t)gateup_brow(r, n0, I) * d; },
+           p.xs, [&](int r) { return p.xs + (size_t)row_token(s, rt.r0 + min(r, last)) * (d / 32); },
+           w1s, [&](int r) { return w1s + (size_t)gateup_brow(r, n0, I) * (d / 32); });
     v16f acc[F][2];
-    mainloop<F, kStages>(lds, L, d / KS, true, acc);
+    mainloop<F, kStages>(lds, L, d / KS, acc);
     gateup_epilogue<F>(acc, rt.r0, rt.rows, n0, I, p.g, p.u, p.hq, p.hs);
   });
 }
@@ -66,9 +76,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_down(DownArgs p) {
   const int I = p.I, d = p.d, NT = (d + TN - 1) / TN;
   int item;
   if (!xcd_item(s.tile_start[s.n_exp] * NT, &item)) return;
-  const RowTile rt = row_tile(s, item / NT);
+  int nt;
+  const RowTile rt = item_tile(s, item, NT, &nt);
   if (rt.rows <= 0) return;
-  const int n0 = (item % NT) * TN;
+  const int n0 = nt * TN;
   const uint8_t* w2 = p.w2q + (size_t)rt.e * d * I;
   const uint8_t* w2s = p.w2s + (size_t)rt.e * d * (I / 32);
   const int last = rt.rows - 1;
@@ -76,18 +87,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_down(DownArgs p) {
   const bool active = n0 + 64 * w < d;
   dispatch_rows(rt.rows, [&]<int F>() {
     TileLoads<F> L;
-    L.init([&](int r) { return p.hq + (size_t)(rt.r0 + min(r, last)) * I; },
-           [&](int r) { return w2 + (size_t)min(n0 + r, d - 1) * I; },
-           [&](int r) { return p.hs + (size_t)(rt.r0 + min(r, last)) * (I / 32); },
-           [&](int r) { return w2s + (size_t)min(n0 + r, d - 1) * (I / 32); });
+    const uint8_t* ha = p.hq + (size_t)rt.r0 * I;
+    const uint8_t* hsa = p.hs + (size_t)rt.r0 * (I / 32);
+    L.init(ha, [&](int r) { return ha + (size_t)min(r, last) * I; },
+           w2, [&](int r) { return w2 + (size_t)min(n0 + r, d - 1) * I; },
+           hsa, [&](int r) { return hsa + (size_t)min(r, last) * (I / 32); },
+           w2s, [&](int r) { return w2s + (size_t)min(n0 + r, d - 1) * (I / 32); });
     v16f acc[F][2];
-    mainloop<F, kStages>(lds, L, I / KS, active, acc);
+    mainloop<F, kStages>(lds, L, I / KS, acc);
+    const int64_t* slot = row_slot_table(s, rt, lds + ((I / KS) % kStages) * STAGE_BYTES);
     if (!active) return;
     static_for<F>([&]<int mi>() {
       static_for<16>([&]<int v>() {
         const int r = 32 * mi + 8 * (v >> 2) + 4 * h + (v & 3);
         if (r < rt.rows) {
-          float* dst = p.yslot + row_slot(s, rt.r0 + r) * d + n0 + 64 * w + i;
+          float* dst = p.yslot + slot[r] * d + n0 + 64 * w + i;
           dst[0] = acc[mi][0][v];
           dst[32] = acc[mi][1][v];
         }
@@ -107,9 +121,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_down(DgradDownArgs p) {
   const int I = p.I, d = p.d, NT = (I + TN - 1) / TN;
   int item;
   if (!xcd_item(s.tile_start[s.n_exp] * NT, &item)) return;
-  const RowTile rt = row_tile(s, item / NT);
+  int nt;
+  const RowTile rt = item_tile(s, item, NT, &nt);
   if (rt.rows <= 0) return;
-  const int n0 = (item % NT) * TN;
+  const int n0 = nt * TN;
   const uint8_t* w2t = p.w2tq + (size_t)rt.e * I * d;
   const uint8_t* w2ts = p.w2ts + (size_t)rt.e * I * (d / 32);
   const int last = rt.rows - 1;
@@ -117,12 +132,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_down(DgradDownArgs p) {
   const bool active = n0 + 64 * w < I;
   dispatch_rows(rt.rows, [&]<int F>() {
     TileLoads<F> L;
-    L.init([&](int r) { return p.dyq + (size_t)row_token(s, rt.r0 + min(r, last)) * d; },
-           [&](int r) { return w2t + (size_t)min(n0 + r, I - 1) * d; },
-           [&](int r) { return p.dys + (size_t)row_token(s, rt.r0 + min(r, last)) * (d / 32); },
-           [&](int r) { return w2ts + (size_t)min(n0 + r, I - 1) * (d / 32); });
+    L.init(p.dyq, [&](int r) { return p.dyq + (size_t)row_token(s, rt.r0 + min(r, last)) * d; },
+           w2t, [&](int r) { return w2t + (size_t)min(n0 + r, I - 1) * d; },
+           p.dys, [&](int r) { return p.dys + (size_t)row_token(s, rt.r0 + min(r, last)) * (d / 32); },
+           w2ts, [&](int r) { return w2ts + (size_t)min(n0 + r, I - 1) * (d / 32); });
     v16f acc[F][2];
-    mainloop<F, kStages>(lds, L, d / KS, active, acc);
+    mainloop<F, kStages>(lds, L, d / KS, acc);
+    // combine weight of every row of the tile, once, through LDS
+    float* wt = (float*)(lds + ((d / KS) % kStages) * STAGE_BYTES);
+    if ((int)threadIdx.x < rt.rows) wt[threadIdx.x] = row_weight(s, p.w, rt.r0 + threadIdx.x);
+    __syncthreads();
     if (!active) return;
     const int I2 = 2 * I;
     static_for<F>([&]<int mi>() {
@@ -130,7 +149,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_down(DgradDownArgs p) {
       float gv[2][16], uv[2][16], wv[16];
       static_for<16>([&]<int v>() {
         const int rg = rt.r0 + min(32 * mi + 8 * (v >> 2) + 4 * h + (v & 3), last);
-        wv[v] = row_weight(s, p.w, rg);
+        wv[v] = wt[rg - rt.r0];
         static_for<2>([&]<int ni>() {
           const size_t o = (size_t)rg * I + n0 + 64 * w + 32 * ni + i;
           gv[ni][v] = p.g[o];
@@ -176,9 +195,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_gateup(DgradGateUpArgs p)
   const int I2 = 2 * p.I, d = p.d, NT = (d + TN - 1) / TN;
   int item;
   if (!xcd_item(s.tile_start[s.n_exp] * NT, &item)) return;
-  const RowTile rt = row_tile(s, item / NT);
+  int nt;
+  const RowTile rt = item_tile(s, item, NT, &nt);
   if (rt.rows <= 0) return;
-  const int n0 = (item % NT) * TN;
+  const int n0 = nt * TN;
   const uint8_t* w1t = p.w1tq + (size_t)rt.e * d * I2;
   const uint8_t* w1ts = p.w1ts + (size_t)rt.e * d * (I2 / 32);
   const int last = rt.rows - 1;
@@ -186,18 +206,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_gateup(DgradGateUpArgs p)
   const bool active = n0 + 64 * w < d;
   dispatch_rows(rt.rows, [&]<int F>() {
     TileLoads<F> L;
-    L.init([&](int r) { return p.dguq + (size_t)(rt.r0 + min(r, last)) * I2; },
-           [&](int r) { return w1t + (size_t)min(n0 + r, d - 1) * I2; },
-           [&](int r) { return p.dgus + (size_t)(rt.r0 + min(r, last)) * (I2 / 32); },
-           [&](int r) { return w1ts + (size_t)min(n0 + r, d - 1) * (I2 / 32); });
+    const uint8_t* ga = p.dguq + (size_t)rt.r0 * I2;
+    const uint8_t* gsa = p.dgus + (size_t)rt.r0 * (I2 / 32);
+    L.init(ga, [&](int r) { return ga + (size_t)min(r, last) * I2; },
+           w1t, [&](int r) { return w1t + (size_t)min(n0 + r, d - 1) * I2; },
+           gsa, [&](int r) { return gsa + (size_t)min(r, last) * (I2 / 32); },
+           w1ts, [&](int r) { return w1ts + (size_t)min(n0 + r, d - 1) * (I2 / 32); });
     v16f acc[F][2];
-    mainloop<F, kStages>(lds, L, I2 / KS, active, acc);
+    mainloop<F, kStages>(lds, L, I2 / KS, acc);
+    const int64_t* slot = row_slot_table(s, rt, lds + ((I2 / KS) % kStages) * STAGE_BYTES);
     if (!active) return;
     static_for<F>([&]<int mi>() {
       static_for<16>([&]<int v>() {
         const int r = 32 * mi + 8 * (v >> 2) + 4 * h + (v & 3);
         if (r < rt.rows) {
-          float* dst = p.dxslot + row_slot(s, rt.r0 + r) * d + n0 + 64 * w + i;
+          float* dst = p.dxslot + slot[r] * d + n0 + 64 * w + i;
           dst[0] = acc[mi][0][v];
           dst[32] = acc[mi][1][v];
         }
@@ -209,13 +232,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_gateup(DgradGateUpArgs p)
 // ---------------------------------------------------------------------------------------------
 // Weight gradients: dW_e[m, n] = sum over the expert's tokens of At[m, tok] Bt[n, tok], both
 // operands requantised along the token axis and stored token-contiguous at the expert's padded
-// offset.  An expert with no tokens writes zeros.  Tiles are 128 x 256 with a two-deep
-// pipeline: the token count is short, the tile is store-bound, and the smaller footprint lets
-// two workgroups share a CU so that one's stores overlap the other's loads.
+// offset.  An expert with no tokens writes zeros.  Tiles are 128 x 256 (the token count is
+// short and the tile is store-bound: fewer registers, more workgroups).
 
 constexpr int kWgradF = 4;
 
-__global__ __launch_bounds__(256, 2) void k_gemm_wgrad(WgradArgs p) {
+__global__ __launch_bounds__(256, 1) void k_gemm_wgrad(WgradArgs p) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int MT = p.M / (32 * kWgradF), NT = (p.N + TN - 1) / TN;
   int item;
@@ -228,12 +250,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wgrad(WgradArgs p) {
   const int w = threadIdx.x >> 6, l = lane_id(), i = l & 31, h = l >> 5;
   const bool active = n0 + 64 * w < p.N;
   TileLoads<kWgradF> L;
-  L.init([&](int r) { return p.at + (size_t)(m0 + min(r, 32 * kWgradF - 1)) * ld + k0; },
-         [&](int r) { return p.bt + (size_t)min(n0 + r, p.N - 1) * ld + k0; },
-         [&](int r) { return p.ats + (size_t)(m0 + min(r, 32 * kWgradF - 1)) * (ld / 32) + k0 / 32; },
-         [&](int r) { return p.bts + (size_t)min(n0 + r, p.N - 1) * (ld / 32) + k0 / 32; });
+  const uint8_t* at = p.at + (size_t)m0 * ld + k0;
+  const uint8_t* bt = p.bt + (size_t)n0 * ld + k0;
+  const uint8_t* ats = p.ats + (size_t)m0 * (ld / 32) + k0 / 32;
+  const uint8_t* bts = p.bts + (size_t)n0 * (ld / 32) + k0 / 32;
+  L.init(at, [&](int r) { return at + (size_t)min(r, 32 * kWgradF - 1) * ld; },
+         bt, [&](int r) { return bt + (size_t)(min(n0 + r, p.N - 1) - n0) * ld; },
+         ats, [&](int r) { return ats + (size_t)min(r, 32 * kWgradF - 1) * (ld / 32); },
+         bts, [&](int r) { return bts + (size_t)(min(n0 + r, p.N - 1) - n0) * (ld / 32); });
   v16f acc[kWgradF][2];
-  mainloop<kWgradF, 2>(lds, L, K / KS, active, acc);
+  mainloop<kWgradF, 2>(lds, L, K / KS, acc);
   if (!active) return;
   float* out = p.dw + (size_t)e * p.M * p.N;
   static_for<kWgradF>([&]<int mi>() {

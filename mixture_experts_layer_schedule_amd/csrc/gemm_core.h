@@ -16,13 +16,14 @@
 // ragged row count shortens every wave's work equally.  The accumulators (F x 2 MFMA tiles)
 // stay in registers for the whole K loop.
 //
-// K pipeline: stages of 64 (one MFMA step) in an NST-deep ring of LDS buffers, filled by
-// direct-to-LDS loads (global_load_lds_dwordx4: no registers in between), so NST - 1 stages
-// are in flight while one is multiplied.  Each staged row is 64 bytes; its four 16-byte chunks
-// are XOR-swizzled by the row index so that the fragment reads (lane i reads row i) hit
-// distinct banks.  Scales travel the same way, one 4-byte word per row every other stage.
-// One barrier per stage: it publishes the stage every wave loaded a share of and retires the
-// buffer that the next loads overwrite.
+// K pipeline: stages of 128 (two MFMA steps) in an NST-deep ring of LDS buffers, filled by
+// direct-to-LDS loads (global_load_lds_dwordx4: no registers in between) while the previous
+// stage is multiplied.  A load instruction moves 8 whole staged rows of 128 bytes, so every
+// request is a full cache line.  Each staged row's eight 16-byte chunks are XOR-swizzled by the
+// row index so that the fragment reads (lane i reads row i) hit distinct banks.  Scales travel
+// the same way, one 4-byte word (4 K blocks) per row and stage.  One barrier per stage: it
+// publishes the stage every wave loaded a share of and retires the buffer that the next loads
+// overwrite.
 //
 // Each output tile is owned by exactly one workgroup and K is summed in a fixed order, so
 // results are bitwise reproducible.
@@ -35,20 +36,20 @@ namespace {
 
 constexpr int TM = 256;                      // rows of a full tile (8 fragments of 32)
 constexpr int TN = 256;                      // columns of a tile (4 waves x 64)
-constexpr int KS = 64;                       // K per pipeline stage
+constexpr int KS = 128;                      // K per pipeline stage (two MFMA steps)
 constexpr int A_STAGE = TM * KS;             // bytes of one staged A slice
-constexpr int STAGE_BYTES = (TM + TN) * KS;  // A then B
-constexpr int EPOCH_BYTES = (TM + TN) * 4;   // one scale word (4 K blocks) per row
-constexpr int NEPOCH = 3;                    // scale-word buffers
+constexpr int DATA_BYTES = (TM + TN) * KS;   // A then B
+constexpr int SCALE_BYTES = (TM + TN) * 4;   // one scale word (4 K blocks) per row
+constexpr int STAGE_BYTES = DATA_BYTES + SCALE_BYTES;
 
-constexpr size_t lds_bytes_for(int nst) { return (size_t)nst * STAGE_BYTES + NEPOCH * EPOCH_BYTES; }
+constexpr size_t lds_bytes_for(int nst) { return (size_t)nst * STAGE_BYTES; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Physical 16-byte chunk slot of logical chunk g in staged row r is g ^ swz(r).  For any 16
-// consecutive rows (and any 8), rows with equal r % 4 (r % 2) get distinct slots, so the
-// fragment reads are conflict-free whether the LDS serves 16 or 8 lanes per cycle.
-MOE_DEV int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+// Physical 16-byte chunk slot of logical chunk g in staged row r is g ^ swz(r).  Rows with
+// equal r % 2 among any 16 consecutive rows, and any 8 consecutive rows, get distinct slots, so
+// the fragment reads are conflict-free whether the LDS serves 16 or 8 lanes per cycle.
+MOE_DEV int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
 // Which expert a tile belongs to, from a prefix table of tiles per expert.
 MOE_DEV int tile_expert(const int32_t* tile_start, int n_exp, int tile) {
@@ -63,7 +64,8 @@ MOE_DEV int tile_expert(const int32_t* tile_start, int n_exp, int tile) {
 // Rows [r0, r0 + rows) of expert e covered by its m-th row tile.  An expert with c rows has
 // ceil(c / 256) tiles; the rows are split evenly between them in multiples of 32, so a 300-row
 // expert runs as two 160-row tiles rather than 256 + 44.  rows <= 0 only for experts of more
-// than 2048 rows, whose last tile can come out empty.
+// than 2048 rows, whose last tile can come out empty.  (A wider tile would need more than the
+// 256 accumulator registers per lane.)
 struct RowTile {
   int e, r0, rows;
 };
@@ -77,6 +79,18 @@ MOE_DEV RowTile row_tile(const SchedView& s, int tile) {
   t.r0 = s.offsets[t.e] + m * per;
   t.rows = min(per, c - m * per);
   return t;
+}
+
+// Item `item` of a routed grouped GEMM with NT column tiles.  The items of one expert are
+// ordered column tile major, row tile minor, so the row tiles that share a weight slice are
+// neighbours (their weight reads meet in L2) and a row tile's column tiles lie within 2 x NT
+// consecutive items (their A reads meet in L2 too).  Returns the row tile and the column tile.
+MOE_DEV RowTile item_tile(const SchedView& s, int item, int NT, int* n) {
+  const int e = tile_expert(s.tile_start, s.n_exp, item / NT);
+  const int nm = s.tile_start[e + 1] - s.tile_start[e];
+  const int j = item - s.tile_start[e] * NT;
+  *n = j / nm;
+  return row_tile(s, s.tile_start[e] + j % nm);
 }
 
 // Work item of a grouped launch.  Blocks are dealt round-robin to the 8 XCDs, so the linear
@@ -113,35 +127,36 @@ MOE_DEV float row_weight(const SchedView& s, const float* w, int r) {
   return r < s.R ? w[s.perm[r]] : 1.0f;
 }
 
-// Per-thread source addresses of the direct-to-LDS loads of one tile.  Staged rows are filled
-// 16 per wave instruction: instruction q (wave q % 4) covers rows [16q, 16q + 16), lane l the
-// row 16q + l / 4, chunk slot l % 4.  a_rows(r) / b_rows(r) return the K data of staged row r
-// (callers clamp rows past the operand to a valid one; such rows are never stored) and
-// a_srows / b_srows its scale bytes.
+// Per-thread source addresses of the direct-to-LDS loads of one tile, as 32-bit byte offsets
+// from wave-uniform bases (the loads then take a scalar base and one offset register each).
+// Staged rows are filled 8 per wave instruction: instruction q (wave q % 4) covers rows
+// [8q, 8q + 8), lane l the row 8q + l / 8, chunk slot l % 8.  a_rows(r) / b_rows(r) return the
+// K data of staged row r (callers clamp rows past the operand to a valid one; such rows are
+// never stored) and a_srows / b_srows its scale bytes; every operand lies within 4 GiB of its
+// base.
 template <int F>
 struct TileLoads {
-  static constexpr int NA = (F + 1) / 2;  // A instructions per wave and stage (2F over 4 waves)
-  const uint8_t* a[NA];
-  const uint8_t* b[4];
-  const uint8_t* as;
-  const uint8_t* bs;
+  const uint8_t *abase, *bbase, *asbase, *bsbase;
+  uint32_t a[F];   // A: 4F instructions per stage, F per wave
+  uint32_t b[8];   // B: 32 instructions per stage, 8 per wave
+  uint32_t as, bs;       // scale words of rows 64w + l
 
   template <class ARow, class BRow, class ASRow, class BSRow>
-  MOE_DEV void init(ARow a_rows, BRow b_rows, ASRow a_srows, BSRow b_srows) {
+  MOE_DEV void init(const uint8_t* ab, ARow a_rows, const uint8_t* bb, BRow b_rows, const uint8_t* asb,
+                    ASRow a_srows, const uint8_t* bsb, BSRow b_srows) {
+    abase = ab; bbase = bb; asbase = asb; bsbase = bsb;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int sub = l >> 2, slot = l & 3;
-#pragma unroll
-    for (int u = 0; u < NA; ++u) {
-      const int r = 16 * (w + 4 * u) + sub;  // for odd F the last rows are filled, never read
-      a[u] = a_rows(r) + 16 * (slot ^ swz(r));
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = 16 * (w + 4 * u) + sub;
-      b[u] = b_rows(r) + 16 * (slot ^ swz(r));
-    }
-    as = a_srows(64 * w + l);
-    bs = b_srows(64 * w + l);
+    const int sub = l >> 3, slot = l & 7;
+    static_for<F>([&]<int u>() {
+      const int r = 8 * (w + 4 * u) + sub;
+      a[u] = (uint32_t)(a_rows(r) - ab) + 16 * (slot ^ swz(r));
+    });
+    static_for<8>([&]<int u>() {
+      const int r = 8 * (w + 4 * u) + sub;
+      b[u] = (uint32_t)(b_rows(r) - bb) + 16 * (slot ^ swz(r));
+    });
+    as = (uint32_t)(a_srows(64 * w + l) - asb);
+    bs = (uint32_t)(b_srows(64 * w + l) - bsb);
   }
 };
 
@@ -154,23 +169,20 @@ MOE_DEV void lds_load4(const uint8_t* src, uint8_t* dst) {
   __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)dst, 4, 0, AUX);
 }
 
-// Loads of stage t (K offset 64t) into its buffer; even stages also bring the scale words of
-// K range [64t, 64t + 128).  AUX_A: cache-policy bits of the A loads (16 = sc1: device-coherent
-// reads of rows that other workgroups of the same kernel wrote).
+// Loads of stage t (K range [128t, 128t + 128)) into buffer t % NST: F + 8 data instructions
+// and 2 scale words per wave.  AUX_A: cache-policy bits of the A loads (16 = sc1:
+// device-coherent reads of rows that other workgroups of the same kernel wrote).
 template <int F, int NST, int AUX_A>
 MOE_DEV void issue_stage(const TileLoads<F>& L, uint8_t* lds, int t) {
   const int w = threadIdx.x >> 6;
   const int k0 = t * KS;
   uint8_t* st = lds + (t % NST) * STAGE_BYTES;
-  if ((t & 1) == 0) {
-    uint8_t* ep = lds + NST * STAGE_BYTES + ((t >> 1) % NEPOCH) * EPOCH_BYTES;
-    lds_load4<AUX_A>(L.as + (k0 >> 5), ep + 256 * w);
-    lds_load4<0>(L.bs + (k0 >> 5), ep + TM * 4 + 256 * w);
-  }
-#pragma unroll
-  for (int u = 0; u < TileLoads<F>::NA; ++u) lds_load16<AUX_A>(L.a[u] + k0, st + 1024 * (w + 4 * u));
-#pragma unroll
-  for (int u = 0; u < 4; ++u) lds_load16<0>(L.b[u] + k0, st + A_STAGE + 1024 * (w + 4 * u));
+  uint8_t* sc = st + DATA_BYTES;
+  const uint32_t ks = (uint32_t)k0 >> 5;
+  lds_load4<AUX_A>(L.asbase + (L.as + ks), sc + 256 * w);
+  lds_load4<0>(L.bsbase + (L.bs + ks), sc + TM * 4 + 256 * w);
+  static_for<F>([&]<int u>() { lds_load16<AUX_A>(L.abase + (L.a[u] + (uint32_t)k0), st + 1024 * (w + 4 * u)); });
+  static_for<8>([&]<int u>() { lds_load16<0>(L.bbase + (L.b[u] + (uint32_t)k0), st + A_STAGE + 1024 * (w + 4 * u)); });
 }
 
 // Wait until at most N of this wave's loads are outstanding, then meet the other waves.  The
@@ -180,65 +192,70 @@ MOE_DEV void wait_loads_and_sync() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// Multiply one staged K slice: acc[mi][ni] += A_frag(mi) * B_frag(ni).  sa/sb hold this lane's
-// scale words (already shifted to its K block h); p selects the stage's half of the word.
+// Multiply one staged K slice (two MFMA steps): acc[mi][ni] += A_frag(mi) * B_frag(ni).
+// Staged row 32m + i (B: 64w + 32m + i) has swizzle swz(i) ^ 4(m & 1).  The A fragments are
+// read two at a time, one pair ahead of the matrix instructions that use the previous pair
+// (scheduling barriers keep that order): LDS returns in order, so each instruction waits only
+// for its own operands while the next pair is arriving, and few registers hold fragments.
 template <int F>
-MOE_DEV void compute_stage(const uint8_t* st, const uint32_t (&sa)[F], const uint32_t (&sb)[2], int p,
-                           v16f (&acc)[F][2]) {
+MOE_DEV void compute_stage(const uint8_t* st, v16f (&acc)[F][2]) {
   const int l = lane_id(), i = l & 31, h = l >> 5, w = threadIdx.x >> 6;
-  const int o_lo = 16 * (h ^ swz(i)), o_hi = 16 * ((2 + h) ^ swz(i));
-  v8i b[2];
-#pragma unroll
-  for (int ni = 0; ni < 2; ++ni) {
-    const uint8_t* rp = st + A_STAGE + (64 * w + 32 * ni + i) * KS;
-    const v4i lo = *(const v4i*)(rp + o_lo), hi = *(const v4i*)(rp + o_hi);
-    b[ni] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  }
-  const int sh = 16 * p;
-  const int sb0 = (int)(sb[0] >> sh), sb1 = (int)(sb[1] >> sh);
-  static_for<F>([&]<int mi>() {
-    const uint8_t* rp = st + (32 * mi + i) * KS;
-    const v4i lo = *(const v4i*)(rp + o_lo), hi = *(const v4i*)(rp + o_hi);
-    const v8i a = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    const int s_a = (int)(sa[mi] >> sh);
-    acc[mi][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b[0], acc[mi][0], 0, 0, 0, s_a, 0, sb0);
-    acc[mi][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b[1], acc[mi][1], 0, 0, 0, s_a, 0, sb1);
+  const int sw = swz(i);
+  const uint32_t* sc = (const uint32_t*)(st + DATA_BYTES);
+  int sa[F], sb[2];
+  static_for<F>([&]<int mi>() { sa[mi] = (int)(sc[32 * mi + i] >> (8 * h)); });
+  sb[0] = (int)(sc[TM + 64 * w + i] >> (8 * h));
+  sb[1] = (int)(sc[TM + 64 * w + 32 + i] >> (8 * h));
+  constexpr int NG = (F + 1) / 2;
+  static_for<2>([&]<int kk>() {
+    auto frag = [&](const uint8_t* rp, int s2) {
+      const v4i lo = *(const v4i*)(rp + 16 * ((4 * kk + h) ^ s2));
+      const v4i hi = *(const v4i*)(rp + 16 * ((4 * kk + 2 + h) ^ s2));
+      return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    const v8i b0 = frag(st + A_STAGE + (64 * w + i) * KS, sw);
+    const v8i b1 = frag(st + A_STAGE + (64 * w + 32 + i) * KS, sw ^ 4);
+    v8i pair[NG + 1][2];
+    static_for<2>([&]<int j>() {
+      if constexpr (j < F) pair[0][j] = frag(st + (32 * j + i) * KS, sw ^ (4 * (j & 1)));
+    });
+    static_for<NG>([&]<int g>() {
+      static_for<2>([&]<int j>() {
+        constexpr int mi = 2 * (g + 1) + j;
+        if constexpr (mi < F) pair[g + 1][j] = frag(st + (32 * mi + i) * KS, sw ^ (4 * (mi & 1)));
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<2>([&]<int j>() {
+        constexpr int mi = 2 * g + j;
+        if constexpr (mi < F) {
+          const int s_a = sa[mi] >> (16 * kk);
+          acc[mi][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pair[g][j], b0, acc[mi][0], 0, 0, 0, s_a, 0,
+                                                                        sb[0] >> (16 * kk));
+          acc[mi][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pair[g][j], b1, acc[mi][1], 0, 0, 0, s_a, 0,
+                                                                        sb[1] >> (16 * kk));
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
   });
 }
 
-// acc = A_tile * B_tile^T over K = 64 * nk.  active (wave-uniform): this wave's columns exist;
-// an inactive wave still loads its share and meets every barrier.
-// Loads per wave and stage: NA + 4 data instructions, plus 2 scale words on even stages.
+// acc = A_tile * B_tile^T over K = 128 * nk.  Every wave multiplies, also one whose columns lie
+// past N (its B rows are clamped copies and its results are dropped): a branch around the
+// matrix instructions would make the accumulators change register class every iteration.
 template <int F, int NST, int AUX_A = 0>
-MOE_DEV void mainloop(uint8_t* lds, const TileLoads<F>& L, int nk, bool active, v16f (&acc)[F][2]) {
-  static_assert(NST >= 2 && NST <= 4, "pipeline depth");
-  constexpr int LD = TileLoads<F>::NA + 4;  // data loads of one stage
+MOE_DEV void mainloop(uint8_t* lds, const TileLoads<F>& L, int nk, v16f (&acc)[F][2]) {
+  static_assert(NST == 2, "two LDS stages");
   static_for<F>([&]<int mi>() {
     acc[mi][0] = (v16f){};
     acc[mi][1] = (v16f){};
   });
-  const int w = threadIdx.x >> 6, l = lane_id(), i = l & 31, h = l >> 5;
-  for (int t = 0; t < NST - 1 && t < nk; ++t) issue_stage<F, NST, AUX_A>(L, lds, t);
-  uint32_t sa[F], sb[2];
+  if (nk <= 0) return;
+  issue_stage<F, NST, AUX_A>(L, lds, 0);
   for (int t = 0; t < nk; ++t) {
-    // this wave's loads of stages t+1 .. t+ahead may stay in flight
-    const int ahead = min(nk - 1 - t, NST - 2);
-    if (NST == 4 && ahead == 2) {
-      wait_loads_and_sync<2 * LD + 2>();  // one of the two stages is even (+2 scale words)
-    } else if (ahead == 1) {
-      if ((t + 1) & 1) wait_loads_and_sync<LD>();
-      else wait_loads_and_sync<LD + 2>();
-    } else {
-      wait_loads_and_sync<0>();
-    }
-    if (t + NST - 1 < nk) issue_stage<F, NST, AUX_A>(L, lds, t + NST - 1);
-    if ((t & 1) == 0) {
-      const uint32_t* ep = (const uint32_t*)(lds + NST * STAGE_BYTES + ((t >> 1) % NEPOCH) * EPOCH_BYTES);
-      static_for<F>([&]<int mi>() { sa[mi] = ep[32 * mi + i] >> (8 * h); });
-      sb[0] = ep[TM + 64 * w + i] >> (8 * h);
-      sb[1] = ep[TM + 64 * w + 32 + i] >> (8 * h);
-    }
-    if (active) compute_stage<F>(lds + (t % NST) * STAGE_BYTES, sa, sb, t & 1, acc);
+    wait_loads_and_sync<0>();  // stage t has landed; every wave is done with stage t - 1
+    if (t + 1 < nk) issue_stage<F, NST, AUX_A>(L, lds, t + 1);
+    compute_stage<F>(lds + (t % NST) * STAGE_BYTES, acc);
   }
 }
 

@@ -64,12 +64,12 @@ MOE_DEV void ring_tile(const RingArgs& p, uint8_t* lds, const uint8_t* ring, con
   const uint8_t* w1s = p.w1s + (size_t)rt.e * 2 * I * (d / 32);
   const int last = rt.rows - 1;
   TileLoads<F> L;
-  L.init([&](int r) { return ring + (size_t)min(r, last) * d; },
-         [&](int r) { return w1 + (size_t)gateup_brow(r, n0, I) * d; },
-         [&](int r) { return rings + (size_t)min(r, last) * (d / 32); },
-         [&](int r) { return w1s + (size_t)gateup_brow(r, n0, I) * (d / 32); });
+  L.init(ring, [&](int r) { return ring + (size_t)min(r, last) * d; },
+         w1, [&](int r) { return w1 + (size_t)gateup_brow(r, n0, I) * d; },
+         rings, [&](int r) { return rings + (size_t)min(r, last) * (d / 32); },
+         w1s, [&](int r) { return w1s + (size_t)gateup_brow(r, n0, I) * (d / 32); });
   v16f acc[F][2];
-  mainloop<F, 4, 16>(lds, L, d / KS, true, acc);
+  mainloop<F, 2, 16>(lds, L, d / KS, acc);
   gateup_epilogue<F>(acc, rt.r0, rt.rows, n0, I, p.g, p.u, p.hq, p.hs);
 }
 
