@@ -116,59 +116,78 @@ __global__ __launch_bounds__(256) void k_requant_t(const uint8_t* __restrict__ q
 }
 
 
-// [batch][rows][cols] (blocks along cols) -> [batch][cols][rows] (blocks along rows), register
-// version: a lane owns 8 consecutive columns of 32 consecutive rows (one output block per
-// column), so the new block maximum needs no cross-lane traffic.  Loads are 8 bytes per lane and
-// coalesced across the wave; each output column's block is one 32-byte store.  Codes are decoded
-// two at a time by the hardware conversion and scaled by their row's e8m0 factor.
-__global__ __launch_bounds__(256) void k_requant_t_rows32(const uint8_t* __restrict__ q,
-                                                         const uint8_t* __restrict__ s, int64_t rows, int64_t cols,
-                                                         uint8_t* __restrict__ qt, uint8_t* __restrict__ st) {
+// [batch][rows][cols] (blocks along cols) -> [batch][cols][rows] (blocks along rows) on 128 x 128
+// tiles, staged in LDS as fp8 codes (17 KB per tile, so many tiles are in flight per CU).
+// Loads: thread t reads rows 4(t/8) .. +4, columns 16(t%8) .. +16 (8 lanes cover a whole
+// 128-byte line of a row) and writes each column's 4 codes as one LDS word.  Stores: thread t
+// produces output row t/2 (input column), input rows [64 (t%2), +64): two output blocks whose
+// maxima need no cross-lane traffic, written as one 64-byte run.  Codes are decoded two at a
+// time by the hardware conversion (exact for e4m3) and scaled by their e8m0 factor.
+constexpr int RT = 128;
+constexpr int RPITCH = RT + 4;  // bytes per LDS code row: word reads and writes are conflict-light
+
+__global__ __launch_bounds__(256) void k_requant_t128(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s,
+                                                     int64_t rows, int64_t cols, uint8_t* __restrict__ qt,
+                                                     uint8_t* __restrict__ st) {
+  __shared__ __align__(16) uint8_t ct[RT * RPITCH];  // ct[c][r]: code of input (r, c)
+  __shared__ __align__(16) uint8_t sct[4][RT];       // sct[c / 32][r]: scale byte of input (r, c)
   const int64_t b = blockIdx.z;
-  const int64_t c8 = (int64_t)blockIdx.x * 512 + lane_id() * 8;
-  const int64_t r0 = ((int64_t)blockIdx.y * 4 + (threadIdx.x >> 6)) * 32;
-  if (c8 >= cols || r0 >= rows) return;
-  v2i w[32];
-  float sc[32];
-  const uint8_t* src = q + (b * rows + r0) * cols + c8;
-  const uint8_t* ssrc = s + (b * rows + r0) * (cols / 32) + c8 / 32;
+  const int64_t r0 = (int64_t)blockIdx.y * RT, c0 = (int64_t)blockIdx.x * RT;
+  const int t = threadIdx.x;
+  {
+    const int rg = t >> 3, cg = t & 7;
+    v4i w[4];
+    uint32_t sb = 0;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    w[i] = *(const v2i*)(src + (int64_t)i * cols);
-    sc[i] = e8m0_scale(ssrc[(int64_t)i * (cols / 32)]);
+    for (int j = 0; j < 4; ++j) {
+      const int64_t row = b * rows + r0 + 4 * rg + j;
+      w[j] = *(const v4i*)(q + row * cols + c0 + 16 * cg);
+      sb |= (uint32_t)s[row * (cols / 32) + (c0 + 16 * cg) / 32] << (8 * j);
+    }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const int sh = 8 * (m & 3);
+      const uint32_t col4 = (((uint32_t)w[0][m >> 2] >> sh) & 0xFFu) | ((((uint32_t)w[1][m >> 2] >> sh) & 0xFFu) << 8) |
+                            ((((uint32_t)w[2][m >> 2] >> sh) & 0xFFu) << 16) | ((((uint32_t)w[3][m >> 2] >> sh) & 0xFFu) << 24);
+      *(uint32_t*)(ct + (16 * cg + m) * RPITCH + 4 * rg) = col4;
+    }
+    if ((cg & 1) == 0) *(uint32_t*)(&sct[cg >> 1][4 * rg]) = sb;
   }
-  uint8_t* dst = qt + (b * cols + c8) * rows + r0;
-  uint8_t* sdst = st + (b * cols + c8) * (rows / 32) + r0 / 32;
+  __syncthreads();
+  const int c = t >> 1, half = t & 1;
+  const uint32_t* crow = (const uint32_t*)(ct + c * RPITCH + 64 * half);
+  const uint32_t* srow = (const uint32_t*)(&sct[c >> 5][64 * half]);
+  uint8_t* dst = qt + (b * cols + c0 + c) * rows + r0 + 64 * half;
+  uint8_t* sdst = st + (b * cols + c0 + c) * (rows / 32) + (r0 + 64 * half) / 32;
 #pragma unroll
-  for (int jp = 0; jp < 4; ++jp) {   // column pair (2 jp, 2 jp + 1)
-    float f0[32], f1[32];
-    float m0 = 0.0f, m1 = 0.0f;
+  for (int blk = 0; blk < 2; ++blk) {
+    float v[32];
+    float m = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int word = w[i][jp >> 1];
-      v2f p = (jp & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(word, true) : __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
-      f0[i] = p[0] * sc[i];
-      f1[i] = p[1] * sc[i];
-      m0 = fmaxf(m0, fabsf(f0[i]));
-      m1 = fmaxf(m1, fabsf(f1[i]));
+    for (int k = 0; k < 8; ++k) {  // 4 codes of 4 consecutive rows per word
+      const uint32_t codes = crow[8 * blk + k];
+      const uint32_t sc4 = srow[8 * blk + k];
+      const v2f p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, false);
+      const v2f p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, true);
+      v[4 * k + 0] = p0[0] * e8m0_scale(sc4 & 0xFFu);
+      v[4 * k + 1] = p0[1] * e8m0_scale((sc4 >> 8) & 0xFFu);
+      v[4 * k + 2] = p1[0] * e8m0_scale((sc4 >> 16) & 0xFFu);
+      v[4 * k + 3] = p1[1] * e8m0_scale(sc4 >> 24);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) m = fmaxf(m, fabsf(v[4 * k + x]));
     }
+    const uint32_t byte = e8m0_from_amax(m);
+    const float inv = e8m0_inv_scale(byte);
+    v4i o0, o1;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const float* f = h ? f1 : f0;
-      const uint32_t byte = e8m0_from_amax(h ? m1 : m0);
-      const float inv = e8m0_inv_scale(byte);
-      v4i o0, o1;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        o0[k] = (int)pack4_e4m3(f[4 * k] * inv, f[4 * k + 1] * inv, f[4 * k + 2] * inv, f[4 * k + 3] * inv);
-        o1[k] = (int)pack4_e4m3(f[16 + 4 * k] * inv, f[16 + 4 * k + 1] * inv, f[16 + 4 * k + 2] * inv,
-                                f[16 + 4 * k + 3] * inv);
-      }
-      const int64_t col = 2 * jp + h;
-      *(v4i*)(dst + col * rows) = o0;
-      *(v4i*)(dst + col * rows + 16) = o1;
-      sdst[col * (rows / 32)] = (uint8_t)byte;
+    for (int k = 0; k < 4; ++k) {
+      o0[k] = (int)pack4_e4m3(v[4 * k] * inv, v[4 * k + 1] * inv, v[4 * k + 2] * inv, v[4 * k + 3] * inv);
+      o1[k] = (int)pack4_e4m3(v[16 + 4 * k] * inv, v[16 + 4 * k + 1] * inv, v[16 + 4 * k + 2] * inv,
+                              v[16 + 4 * k + 3] * inv);
     }
+    ((v4i*)dst)[2 * blk] = o0;
+    ((v4i*)dst)[2 * blk + 1] = o1;
+    sdst[blk] = (uint8_t)byte;
   }
 }
 
@@ -245,9 +264,9 @@ hipError_t launch_quant_rows(const void* src, int src_f32, int64_t rows, int64_t
 hipError_t launch_requant_t(const uint8_t* q, const uint8_t* s, int64_t batch, int64_t rows, int64_t cols,
                             uint8_t* qt, uint8_t* st, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
-  if (false) {  // register-blocked variant: measured slower on the expert weights (scattered 32-byte stores)
-    dim3 grid((unsigned)((cols + 511) / 512), (unsigned)((rows + 127) / 128), (unsigned)batch);
-    hipLaunchKernelGGL(k_requant_t_rows32, grid, dim3(256), 0, stream, q, s, rows, cols, qt, st);
+  if (rows % RT == 0 && cols % RT == 0) {
+    dim3 grid((unsigned)(cols / RT), (unsigned)(rows / RT), (unsigned)batch);
+    hipLaunchKernelGGL(k_requant_t128, grid, dim3(256), 0, stream, q, s, rows, cols, qt, st);
   } else {
     dim3 grid((unsigned)(cols / TS), (unsigned)(rows / TS), (unsigned)batch);
     hipLaunchKernelGGL(k_requant_t, grid, dim3(256), 0, stream, q, s, rows, cols, qt, st);

@@ -62,14 +62,17 @@ def test_quant_bf16_activations_and_f32_weights():
     assert np.array_equal(s, rs) and np.array_equal(q, rq)
 
 
-def test_requant_transpose():
+@pytest.mark.parametrize("batch,rows,cols", [(3, 192, 128), (2, 256, 384)])
+def test_requant_transpose(batch, rows, cols):
+    """Both tilings: 64 x 64 (shapes that are not multiples of 128) and 128 x 128."""
     torch = _torch()
     import mixture_experts_layer_schedule_amd as moe
 
     rng = np.random.default_rng(2)
-    batch, rows, cols = 3, 192, 128
     w = (rng.standard_normal((batch, rows, cols)) * np.exp2(rng.integers(-8, 8, size=(batch, rows, 1)))).astype(
         np.float32)
+    w[0, :32, :32] = 0.0                      # an all-zero block (scale byte 0) on both sides
+    w[-1, 32:64, :] *= np.float32(2.0 ** -120)  # tiny values: scale bytes near the bottom of the range
     rq, rs = oracle.quantize(w.astype(np.float64), axis=2)
     q = torch.from_numpy(rq).cuda()
     s = torch.from_numpy(rs).cuda()
