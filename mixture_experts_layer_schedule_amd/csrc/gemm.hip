@@ -232,11 +232,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_gateup(DgradGateUpArgs p)
 // ---------------------------------------------------------------------------------------------
 // Weight gradients: dW_e[m, n] = sum over the expert's tokens of At[m, tok] Bt[n, tok], both
 // operands requantised along the token axis and stored token-contiguous at the expert's padded
-// offset.  An expert with no tokens writes zeros.  Tiles are 128 x 256 (the token count is
-// short and the tile is store-bound: fewer registers, more workgroups).
+// offset.  An expert with no tokens writes zeros.  Tiles are 256 x 256 (128 x 256 when M is not
+// a multiple of 256): the token count is short, so a bigger tile amortises each load latency.
 
-constexpr int kWgradF = 4;
-
+template <int kWgradF>
 __global__ __launch_bounds__(256, 1) void k_gemm_wgrad(WgradArgs p) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int MT = p.M / (32 * kWgradF), NT = (p.N + TN - 1) / TN;
@@ -301,9 +300,16 @@ hipError_t launch_gemm_dgrad_gateup(const DgradGateUpArgs& a, int tiles_bound, h
 }
 
 hipError_t launch_gemm_wgrad(const WgradArgs& a, hipStream_t st) {
-  if (a.M % (32 * kWgradF)) return hipErrorInvalidValue;
-  const int blocks = a.n_exp * (a.M / (32 * kWgradF)) * ((a.N + TN - 1) / TN);
-  hipLaunchKernelGGL(k_gemm_wgrad, dim3(blocks), dim3(256), wgrad_lds_bytes(), st, a);
+  // 256-row tiles when M allows (half the workgroups, each with twice the work per load latency)
+  if (a.M % 256 == 0) {
+    const int blocks = a.n_exp * (a.M / 256) * ((a.N + TN - 1) / TN);
+    hipLaunchKernelGGL(k_gemm_wgrad<8>, dim3(blocks), dim3(256), wgrad_lds_bytes(), st, a);
+  } else if (a.M % 128 == 0) {
+    const int blocks = a.n_exp * (a.M / 128) * ((a.N + TN - 1) / TN);
+    hipLaunchKernelGGL(k_gemm_wgrad<4>, dim3(blocks), dim3(256), wgrad_lds_bytes(), st, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -314,7 +320,10 @@ hipError_t gemm_init() {
   if ((e = hipFuncSetAttribute((const void*)k_gemm_down, hipFuncAttributeMaxDynamicSharedMemorySize, bytes))) return e;
   if ((e = hipFuncSetAttribute((const void*)k_gemm_dgrad_down, hipFuncAttributeMaxDynamicSharedMemorySize, bytes))) return e;
   if ((e = hipFuncSetAttribute((const void*)k_gemm_dgrad_gateup, hipFuncAttributeMaxDynamicSharedMemorySize, bytes))) return e;
-  if ((e = hipFuncSetAttribute((const void*)k_gemm_wgrad, hipFuncAttributeMaxDynamicSharedMemorySize,
+  if ((e = hipFuncSetAttribute((const void*)k_gemm_wgrad<8>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)wgrad_lds_bytes())))
+    return e;
+  if ((e = hipFuncSetAttribute((const void*)k_gemm_wgrad<4>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)wgrad_lds_bytes())))
     return e;
   return hipSuccess;
