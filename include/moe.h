@@ -115,8 +115,9 @@ moe_status moe_quantize_mxfp8(const void* src, int src_is_f32, int64_t rows, int
 /* Transposed requantisation: q [batch, rows, cols] fp8 with scales [batch, rows, cols/32]
  * (quantised along cols) is dequantised exactly and quantised again along rows into
  * qt [batch, cols, rows] with st [batch, cols, rows/32].  rows and cols multiples of 64.
- * This is the backward pass's requantisation of transposed operands, applied by moe_bwd to
- * the expert weights; exported for tests. */
+ * This is the backward pass's requantisation of the expert weights (W1 along 2I, W2 along d),
+ * which moe_bwd performs tile by tile inside its dgrad GEMMs with the same arithmetic; the
+ * standalone form is exported for tests and for callers that want the transposed weights. */
 moe_status moe_requant_transpose(const uint8_t* q, const uint8_t* scales, int64_t batch, int64_t rows, int64_t cols,
                                  uint8_t* qt, uint8_t* st, hipStream_t stream);
 
@@ -137,11 +138,13 @@ moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, c
 /* Backward pass for upstream gradient dy [T, d] bf16, reusing `saved` from moe_fwd of the same
  * inputs.  Outputs: dx_bf16 [T, d] and dx_f32 [T, d] float (or NULL); dw_router [E, d] float;
  * dw1 [NX, 2I, d] float and dw2 [NX, d, I] float (same layouts as w1q / w2q).
- * Steps: quantise dy; combine-weight and router gradients; transposed requantisation of the
- * expert weights; dgrad of the down GEMM (rows pulled from dy: reverse-combine) with the SwiGLU
- * backward and quantisation along 2I; dgrad of the gate/up GEMM pushing rows to their
- * (token, slot) (reverse-dispatch); fixed-order reduction of dx; token-axis requantisation of
- * the wgrad operands; weight-gradient GEMMs. */
+ * Steps: quantise dy; combine-weight and router gradients; dgrad of the down GEMM (rows pulled
+ * from dy: reverse-combine) with the SwiGLU backward and quantisation along 2I; dgrad of the
+ * gate/up GEMM pushing rows to their (token, slot) (reverse-dispatch); fixed-order reduction of
+ * dx; token-axis requantisation of the wgrad operands; weight-gradient GEMMs.  The two dgrad
+ * GEMMs requantise their weight tiles along the contraction axis as they load them (W2 along d,
+ * W1 along 2I: the transposed requantisation of the weights), so phase MOE_PH_REQUANT_W is
+ * empty. */
 moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const void* w_router, const uint8_t* w1q,
                    const uint8_t* w1s, const uint8_t* w2q, const uint8_t* w2s, const void* saved, void* dx_bf16,
                    float* dx_f32, float* dw_router, float* dw1, float* dw2, void* workspace, hipStream_t stream);

@@ -91,7 +91,7 @@ moe_saved_layout saved_layout(const Dims& m) {
 }
 
 struct Work {
-  size_t status, ring, ring_s, ring_flags, blkcnt, dyq, dys, dw, dl, w1tq, w1ts, w2tq, w2ts, dguq, dgus, dxslot;
+  size_t status, ring, ring_s, ring_flags, blkcnt, dyq, dys, dw, dl, dguq, dgus, dxslot;
   size_t xt, xts, ht, hts, dyt, dyts, dgut, dguts, total;
 };
 
@@ -107,10 +107,6 @@ Work work_layout(const Dims& m) {
   w.dys = L.take(m.T * m.d / 32);
   w.dw = L.take(4 * m.T * m.k);
   w.dl = L.take(4 * m.T * m.k);
-  w.w1tq = L.take(m.NX * m.d * 2 * m.I);
-  w.w1ts = L.take(m.NX * m.d * 2 * m.I / 32);
-  w.w2tq = L.take(m.NX * m.I * m.d);
-  w.w2ts = L.take(m.NX * m.I * m.d / 32);
   w.dguq = L.take(m.RS * 2 * m.I);
   w.dgus = L.take(m.RS * 2 * m.I / 32);
   w.dxslot = L.take(4 * m.T * (m.k + m.S) * m.d);
@@ -345,21 +341,16 @@ moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const v
   MOE_TRY(launch_router_wgrad(sv, dl, (const uint16_t*)x, d, (int)m.E, dw_router, stream));
   mark(stream, MOE_PH_ROUTER_WGRAD);
 
-  // requantise the expert weights along their other axis: W1 along 2I, W2 along d
-  uint8_t* w1tq = at<uint8_t>(workspace, wl.w1tq);
-  uint8_t* w1ts = at<uint8_t>(workspace, wl.w1ts);
-  uint8_t* w2tq = at<uint8_t>(workspace, wl.w2tq);
-  uint8_t* w2ts = at<uint8_t>(workspace, wl.w2ts);
-  MOE_TRY(launch_requant_t(w1q, w1s, m.NX, 2 * m.I, m.d, w1tq, w1ts, stream));
-  MOE_TRY(launch_requant_t(w2q, w2s, m.NX, m.d, m.I, w2tq, w2ts, stream));
+  // The transposed requantisation of the expert weights (W1 along 2I, W2 along d) happens inside
+  // the two dgrad GEMMs, tile by tile, from w1q / w2q: the phase below is empty.
   mark(stream, MOE_PH_REQUANT_W);
 
   DgradDownArgs dd;
   dd.s = sv;
   dd.dyq = dyq;
   dd.dys = dys;
-  dd.w2tq = w2tq;
-  dd.w2ts = w2ts;
+  dd.w2q = w2q;
+  dd.w2s = w2s;
   dd.w = w;
   dd.g = at<float>(saved, sl.g);
   dd.u = at<float>(saved, sl.u);
@@ -374,8 +365,8 @@ moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const v
   dg.s = sv;
   dg.dguq = dd.dguq;
   dg.dgus = dd.dgus;
-  dg.w1tq = w1tq;
-  dg.w1ts = w1ts;
+  dg.w1q = w1q;
+  dg.w1s = w1s;
   dg.dxslot = at<float>(workspace, wl.dxslot);
   dg.d = d;
   dg.I = I;

@@ -125,19 +125,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_down(DgradDownArgs p) {
   const RowTile rt = item_tile(s, item, NT, &nt);
   if (rt.rows <= 0) return;
   const int n0 = nt * TN;
-  const uint8_t* w2t = p.w2tq + (size_t)rt.e * I * d;
-  const uint8_t* w2ts = p.w2ts + (size_t)rt.e * I * (d / 32);
   const int last = rt.rows - 1;
   const int w = threadIdx.x >> 6, l = lane_id(), i = l & 31, h = l >> 5;
   const bool active = n0 + 64 * w < I;
   dispatch_rows(rt.rows, [&]<int F>() {
     TileLoads<F> L;
     L.init(p.dyq, [&](int r) { return p.dyq + (size_t)row_token(s, rt.r0 + min(r, last)) * d; },
-           w2t, [&](int r) { return w2t + (size_t)min(n0 + r, I - 1) * d; },
+           p.dyq, [&](int) { return p.dyq; },
            p.dys, [&](int r) { return p.dys + (size_t)row_token(s, rt.r0 + min(r, last)) * (d / 32); },
-           w2ts, [&](int r) { return w2ts + (size_t)min(n0 + r, I - 1) * (d / 32); });
+           p.dys, [&](int) { return p.dys; });
+    TransB tb;  // W2t = W2^T requantised along d: K = d rows of W2, N = I columns
+    tb.init(p.w2q + (size_t)rt.e * d * I, p.w2s + (size_t)rt.e * d * (I / 32), I, n0);
     v16f acc[F][2];
-    mainloop<F, kStages>(lds, L, d / KS, acc);
+    mainloop_tb<F>(lds, L, tb, d / KS, acc);
     // combine weight of every row of the tile, once, through LDS
     float* wt = (float*)(lds + ((d / KS) % kStages) * STAGE_BYTES);
     if ((int)threadIdx.x < rt.rows) wt[threadIdx.x] = row_weight(s, p.w, rt.r0 + threadIdx.x);
@@ -199,8 +199,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_gateup(DgradGateUpArgs p)
   const RowTile rt = item_tile(s, item, NT, &nt);
   if (rt.rows <= 0) return;
   const int n0 = nt * TN;
-  const uint8_t* w1t = p.w1tq + (size_t)rt.e * d * I2;
-  const uint8_t* w1ts = p.w1ts + (size_t)rt.e * d * (I2 / 32);
   const int last = rt.rows - 1;
   const int w = threadIdx.x >> 6, l = lane_id(), i = l & 31, h = l >> 5;
   const bool active = n0 + 64 * w < d;
@@ -209,11 +207,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_gateup(DgradGateUpArgs p)
     const uint8_t* ga = p.dguq + (size_t)rt.r0 * I2;
     const uint8_t* gsa = p.dgus + (size_t)rt.r0 * (I2 / 32);
     L.init(ga, [&](int r) { return ga + (size_t)min(r, last) * I2; },
-           w1t, [&](int r) { return w1t + (size_t)min(n0 + r, d - 1) * I2; },
+           ga, [&](int) { return ga; },
            gsa, [&](int r) { return gsa + (size_t)min(r, last) * (I2 / 32); },
-           w1ts, [&](int r) { return w1ts + (size_t)min(n0 + r, d - 1) * (I2 / 32); });
+           gsa, [&](int) { return gsa; });
+    TransB tb;  // W1t = W1^T requantised along 2I: K = 2I rows of W1, N = d columns
+    tb.init(p.w1q + (size_t)rt.e * I2 * d, p.w1s + (size_t)rt.e * I2 * (d / 32), d, n0);
     v16f acc[F][2];
-    mainloop<F, kStages>(lds, L, I2 / KS, acc);
+    mainloop_tb<F>(lds, L, tb, I2 / KS, acc);
     const int64_t* slot = row_slot_table(s, rt, lds + ((I2 / KS) % kStages) * STAGE_BYTES);
     if (!active) return;
     static_for<F>([&]<int mi>() {

@@ -140,6 +140,7 @@ struct TileLoads {
   uint32_t a[F];   // A: 4F instructions per stage, F per wave
   uint32_t b[8];   // B: 32 instructions per stage, 8 per wave
   uint32_t as, bs;       // scale words of rows 64w + l
+  uint32_t bk = KS, bsk = KS / 32;  // bytes between the B data / scale words of successive stages
 
   template <class ARow, class BRow, class ASRow, class BSRow>
   MOE_DEV void init(const uint8_t* ab, ARow a_rows, const uint8_t* bb, BRow b_rows, const uint8_t* asb,
@@ -169,20 +170,31 @@ MOE_DEV void lds_load4(const uint8_t* src, uint8_t* dst) {
   __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)dst, 4, 0, AUX);
 }
 
-// Loads of stage t (K range [128t, 128t + 128)) into buffer t % NST: F + 8 data instructions
-// and 2 scale words per wave.  AUX_A: cache-policy bits of the A loads (16 = sc1:
+// A half of the loads of stage t (K range [128t, 128t + 128)) into buffer t % NST: one scale
+// word and F data instructions per wave.  AUX_A: cache-policy bits of the A loads (16 = sc1:
 // device-coherent reads of rows that other workgroups of the same kernel wrote).
+template <int F, int NST, int AUX_A>
+MOE_DEV void issue_a_stage(const TileLoads<F>& L, uint8_t* lds, int t) {
+  const int w = threadIdx.x >> 6;
+  const int k0 = t * KS;
+  uint8_t* st = lds + (t % NST) * STAGE_BYTES;
+  uint8_t* sc = st + DATA_BYTES;
+  lds_load4<AUX_A>(L.asbase + (L.as + ((uint32_t)k0 >> 5)), sc + 256 * w);
+  static_for<F>([&]<int u>() { lds_load16<AUX_A>(L.abase + (L.a[u] + (uint32_t)k0), st + 1024 * (w + 4 * u)); });
+}
+
+// Loads of stage t into buffer t % NST: 2 scale words, then F + 8 data instructions per wave.
 template <int F, int NST, int AUX_A>
 MOE_DEV void issue_stage(const TileLoads<F>& L, uint8_t* lds, int t) {
   const int w = threadIdx.x >> 6;
   const int k0 = t * KS;
   uint8_t* st = lds + (t % NST) * STAGE_BYTES;
   uint8_t* sc = st + DATA_BYTES;
-  const uint32_t ks = (uint32_t)k0 >> 5;
-  lds_load4<AUX_A>(L.asbase + (L.as + ks), sc + 256 * w);
-  lds_load4<0>(L.bsbase + (L.bs + ks), sc + TM * 4 + 256 * w);
+  lds_load4<AUX_A>(L.asbase + (L.as + ((uint32_t)k0 >> 5)), sc + 256 * w);
+  lds_load4<0>(L.bsbase + (L.bs + (uint32_t)t * L.bsk), sc + TM * 4 + 256 * w);
   static_for<F>([&]<int u>() { lds_load16<AUX_A>(L.abase + (L.a[u] + (uint32_t)k0), st + 1024 * (w + 4 * u)); });
-  static_for<8>([&]<int u>() { lds_load16<0>(L.bbase + (L.b[u] + (uint32_t)k0), st + A_STAGE + 1024 * (w + 4 * u)); });
+  const uint32_t kb = (uint32_t)t * L.bk;
+  static_for<8>([&]<int u>() { lds_load16<0>(L.bbase + (L.b[u] + kb), st + A_STAGE + 1024 * (w + 4 * u)); });
 }
 
 // Wait until at most N of this wave's loads are outstanding, then meet the other waves.  The
@@ -192,13 +204,17 @@ MOE_DEV void wait_loads_and_sync() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// An empty statement that reads and rewrites two accumulator tiles in place: code after it
+// cannot start before the matrix instructions that produce them have been issued.
+MOE_DEV void pin_agprs(v16f& a, v16f& b) { asm volatile("" : "+a"(a), "+a"(b)::"memory"); }
+
 // Multiply one staged K slice (two MFMA steps): acc[mi][ni] += A_frag(mi) * B_frag(ni).
 // Staged row 32m + i (B: 64w + 32m + i) has swizzle swz(i) ^ 4(m & 1).  The A fragments are
 // read two at a time, one pair ahead of the matrix instructions that use the previous pair
 // (scheduling barriers keep that order): LDS returns in order, so each instruction waits only
 // for its own operands while the next pair is arriving, and few registers hold fragments.
-template <int F>
-MOE_DEV void compute_stage(const uint8_t* st, v16f (&acc)[F][2]) {
+template <int F, class Hook>
+MOE_DEV void compute_stage(const uint8_t* st, v16f (&acc)[F][2], const Hook& hook) {
   const int l = lane_id(), i = l & 31, h = l >> 5, w = threadIdx.x >> 6;
   const int sw = swz(i);
   const uint32_t* sc = (const uint32_t*)(st + DATA_BYTES);
@@ -235,9 +251,27 @@ MOE_DEV void compute_stage(const uint8_t* st, v16f (&acc)[F][2]) {
                                                                         sb[1] >> (16 * kk));
         }
       });
+      // independent vector work placed here issues while the matrix core runs the group
+      if constexpr (!Hook::kEmpty) {
+        static_for<2>([&]<int j>() {  // the group's products exist before the hook's code
+          constexpr int mi = 2 * g + j;
+          if constexpr (mi < F) pin_agprs(acc[mi][0], acc[mi][1]);
+        });
+        hook.template operator()<kk * NG + g, 2 * NG>();
+      }
       __builtin_amdgcn_sched_barrier(0);
     });
   });
+}
+
+struct NoHook {
+  static constexpr bool kEmpty = true;
+  template <int G, int NGROUPS>
+  MOE_DEV void operator()() const {}
+};
+template <int F>
+MOE_DEV void compute_stage(const uint8_t* st, v16f (&acc)[F][2]) {
+  compute_stage<F>(st, acc, NoHook{});
 }
 
 // acc = A_tile * B_tile^T over K = 128 * nk.  Every wave multiplies, also one whose columns lie
@@ -256,6 +290,140 @@ MOE_DEV void mainloop(uint8_t* lds, const TileLoads<F>& L, int nk, v16f (&acc)[F
     wait_loads_and_sync<0>();  // stage t has landed; every wave is done with stage t - 1
     if (t + 1 < nk) issue_stage<F, NST, AUX_A>(L, lds, t + 1);
     compute_stage<F>(lds + (t % NST) * STAGE_BYTES, acc);
+  }
+}
+
+// B operand of a dgrad GEMM built in the kernel from a forward weight ("transposed
+// requantisation").  The forward weight Wq of one expert is a K x N code matrix quantised along
+// its rows (blocks of 32 of the N values); the dgrad GEMM contracts over K, so its B tile (N
+// rows, K contiguous, blocks along K) is W^T requantised: every 32 K values of a column are
+// dequantised exactly (e4m3 code x 2^(e - 127) is a float32) and quantised again with the
+// block's own e8m0 exponent, the arithmetic of the standalone requantisation kernel.  Doing it
+// here reads the weight once per tile instead of writing and re-reading a transposed copy.
+//
+// Stage t covers K rows [128t, 128t + 128): wave w requantises K block w (32 rows) of the 256
+// tile columns; lane l holds columns [16 (l % 16), +16) of rows 8 (l / 16) .. +8 of that block,
+// loaded as eight 16-byte pieces (four lanes of a wave instruction share a row, so one
+// instruction reads four whole 256-byte row segments) plus one scale byte per row.  The block
+// maximum of a column spans the four lanes l, l ^ 16, l ^ 32, l ^ 48.  Each column's 8 new codes
+// go to the staged B row as one 8-byte LDS write and its new scale byte to the stage's B scale
+// word (byte w = K block w).
+struct TransB {
+  const uint8_t* q;  // [K][N] codes of the expert
+  const uint8_t* s;  // [K][N / 32] scale bytes
+  int N;
+  uint32_t qoff, soff;  // this lane's first piece / scale byte (K row 32w + 8(l / 16), stage 0)
+  v4i raw[8];           // the stage being requantised: 8 row pieces,
+  float f[8];           // their dequantisation factors 2^(e - 127)
+  v4i nraw[8];          // the next stage, in flight: pieces and scale bytes
+  uint32_t nsraw[8];
+
+  // n0: first column of the tile; columns past N (N a multiple of 128) repeat the last valid
+  // 16 (their results are dropped).
+  MOE_DEV void init(const uint8_t* q_, const uint8_t* s_, int N_, int n0) {
+    q = q_; s = s_; N = N_;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int col = min(n0 + 16 * (l & 15), N - 16);
+    const int row = 32 * w + 8 * (l >> 4);
+    qoff = (uint32_t)row * (uint32_t)N + (uint32_t)col;
+    soff = (uint32_t)row * (uint32_t)(N / 32) + (uint32_t)(col >> 5);
+  }
+
+  // 16 loads per lane into the in-flight set: 8 pieces, then 8 scale bytes.
+  MOE_DEV void load_next(int t) {
+    const uint32_t r0 = (uint32_t)(128 * t);
+    static_for<8>([&]<int j>() { nraw[j] = *(const v4i*)(q + (qoff + (r0 + j) * (uint32_t)N)); });
+    static_for<8>([&]<int j>() { nsraw[j] = s[soff + (r0 + j) * (uint32_t)(N / 32)]; });
+  }
+
+  // The in-flight stage becomes the one to requantise (waits for its loads).
+  MOE_DEV void advance() {
+    static_for<8>([&]<int j>() {
+      raw[j] = nraw[j];
+      f[j] = e8m0_scale(nsraw[j]);
+    });
+  }
+
+  // Requantise column pair P of this lane (word P / 2 of every piece, half P % 2: columns
+  // 16 (l % 16) + 2P, + 1) into stage buffer st.
+  template <int P>
+  MOE_DEV void requant_pair(uint8_t* st) const {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int cg = l & 15, ng = l >> 4;
+    float v[8][2];
+    static_for<8>([&]<int j>() {
+      const v2f x = __builtin_amdgcn_cvt_pk_f32_fp8(raw[j][P >> 1], (P & 1) != 0);
+      v[j][0] = x[0] * f[j];
+      v[j][1] = x[1] * f[j];
+    });
+    static_for<2>([&]<int c>() {
+      float m = 0.0f;
+      static_for<8>([&]<int j>() { m = fmaxf(m, fabsf(v[j][c])); });
+      // maximum over the lanes l ^ 16, l ^ 32, l ^ 48 (the other 24 rows of the block)
+      const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_int(m), __float_as_int(m), false, false);
+      m = fmaxf(__int_as_float(p16[0]), __int_as_float(p16[1]));
+      const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_int(m), __float_as_int(m), false, false);
+      m = fmaxf(__int_as_float(p32[0]), __int_as_float(p32[1]));
+      const uint32_t byte = e8m0_from_amax(m);
+      const float inv = e8m0_inv_scale(byte);
+      v2i codes;
+      codes[0] = (int)pack4_e4m3(v[0][c] * inv, v[1][c] * inv, v[2][c] * inv, v[3][c] * inv);
+      codes[1] = (int)pack4_e4m3(v[4][c] * inv, v[5][c] * inv, v[6][c] * inv, v[7][c] * inv);
+      const int r = 16 * cg + 2 * P + c;  // staged B row = tile column
+      const int chunk = 2 * w + (ng >> 1);
+      *(v2i*)(st + A_STAGE + r * KS + 16 * (chunk ^ swz(r)) + 8 * (ng & 1)) = codes;
+      st[DATA_BYTES + TM * 4 + 4 * r + w] = (uint8_t)byte;  // the 4 lanes of a column write the same byte
+    });
+  }
+
+  template <int P0, int P1>
+  MOE_DEV void requant_pairs(uint8_t* st) const {
+    static_for<P1 - P0>([&]<int p>() { requant_pair<P0 + p>(st); });
+  }
+};
+
+// Spreads the requantisation of the next stage (8 column pairs per lane) over the matrix
+// groups of compute_stage, so that its vector work issues while the matrix core is busy.  No
+// branch: a branch between the groups would let the compiler gather every fragment read ahead
+// of the matrix instructions.
+struct RequantHook {
+  static constexpr bool kEmpty = false;
+  const TransB& tb;
+  uint8_t* st;
+  template <int G, int NGROUPS>
+  MOE_DEV void operator()() const {
+    tb.requant_pairs<8 * G / NGROUPS, 8 * (G + 1) / NGROUPS>(st);
+  }
+};
+
+// mainloop with the B tile requantised in the kernel from a forward weight (TransB).  Stage t:
+// after the barrier the raw B of stage t + 2 and the A of stage t + 1 are loaded, and stage t
+// is multiplied while the raw B of stage t + 1 (loaded during stage t - 1) is requantised into
+// the other buffer between the matrix groups.  One barrier per stage, as in mainloop.
+template <int F>
+MOE_DEV void mainloop_tb(uint8_t* lds, const TileLoads<F>& L, TransB& tb, int nk, v16f (&acc)[F][2]) {
+  static_for<F>([&]<int mi>() {
+    acc[mi][0] = (v16f){};
+    acc[mi][1] = (v16f){};
+  });
+  if (nk <= 0) return;
+  tb.load_next(0);
+  issue_a_stage<F, 2, 0>(L, lds, 0);
+  tb.advance();
+  tb.requant_pairs<0, 8>(lds);
+  if (nk > 1) {
+    tb.load_next(1);
+    tb.advance();
+  }
+  for (int t = 0; t < nk; ++t) {
+    // A of stage t has landed; every wave wrote its share of stage t's B and is done with t - 1
+    wait_loads_and_sync<0>();
+    if (t + 2 < nk) tb.load_next(t + 2);
+    if (t + 1 < nk) issue_a_stage<F, 2, 0>(L, lds, t + 1);
+    // (in the last stage this requantises stale registers into the B region of the free buffer,
+    // which nothing reads afterwards: cheaper than a branch)
+    compute_stage<F>(lds + (t % 2) * STAGE_BYTES, acc, RequantHook{tb, lds + ((t + 1) % 2) * STAGE_BYTES});
+    if (t + 2 < nk) tb.advance();
   }
 }
 

@@ -32,7 +32,8 @@ struct DownArgs {
 
 struct DgradDownArgs {
   SchedView s;
-  const uint8_t *dyq, *dys, *w2tq, *w2ts;
+  const uint8_t *dyq, *dys;
+  const uint8_t *w2q, *w2s;  // forward weight [E+S][d][I] + [E+S][d][I/32], requantised along d in the kernel
   const float *w, *g, *u;
   uint8_t *dguq, *dgus;
   int d, I;
@@ -40,7 +41,8 @@ struct DgradDownArgs {
 
 struct DgradGateUpArgs {
   SchedView s;
-  const uint8_t *dguq, *dgus, *w1tq, *w1ts;
+  const uint8_t *dguq, *dgus;
+  const uint8_t *w1q, *w1s;  // forward weight [E+S][2I][d] + [E+S][2I][d/32], requantised along 2I in the kernel
   float* dxslot;
   int d, I;
 };
