@@ -49,7 +49,7 @@ def phase_work(cfg, tok_pad: int) -> dict:
         "combine": (0.0, R * d * 4 + T * d * (2 + 4)),
         "quant_dy": (0.0, T * d * 2 + T * d * q),
         "router_bwd": (2.0 * T * k * d, T * k * d * 4 + T * d * 2),
-        "requant_w": (0.0, 2 * (w1 + w2)),
+        "requant_w": (0.0, 0.0),  # done inside the dgrad GEMMs (their bytes count the weights once)
         "dgrad_down": (2.0 * R * d * I, w2 + R * d * q + R * I * 8 + R * 2 * I * q),
         "dgrad_gateup": (2.0 * R * 2 * I * d, w1 + R * 2 * I * q + R * d * 4),
         "dx_reduce": (0.0, R * d * 4 + T * d * 6),
@@ -86,7 +86,7 @@ class PhaseEvents:
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dsv3_fwd_bwd_hbm_traffic.txt")
 PHASE_DISPATCHES = {  # phase -> kernel dispatches of one step (name#index in launch order)
     "gateup": ["k_gemm_gateup#0"], "down": ["k_gemm_down#0"], "combine": ["k_combine#0"],
-    "router_bwd": ["k_router_bwd#0"], "requant_w": ["k_requant_t#0", "k_requant_t#1"],
+    "router_bwd": ["k_router_bwd#0"],
     "dgrad_down": ["k_gemm_dgrad_down#0"], "dgrad_gateup": ["k_gemm_dgrad_gateup#0"],
     "dx_reduce": ["k_dx_reduce#0"], "wgrad_down": ["k_gemm_wgrad#0"], "wgrad_gateup": ["k_gemm_wgrad#1"],
 }
@@ -246,32 +246,41 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done")
 
-    phase_ms = {p: 0.0 for p in moe.PHASES}
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    total_ms = 0.0
-    for i in range(args.steps):
-        start.record(stream)
-        step()
-        stop.record(stream)
-        stop.synchronize()
-        total_ms += start.elapsed_time(stop)
-        prev = None
-        for p, name in enumerate(moe.PHASES):
-            if name in ("fwd_begin", "bwd_begin"):
+    def timed(n):
+        """n steps bracketed by events; returns (ms per step, per-phase ms from the library's marks)."""
+        pms = {p: 0.0 for p in moe.PHASES}
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        total = 0.0
+        for i in range(n):
+            start.record(stream)
+            step()
+            stop.record(stream)
+            stop.synchronize()
+            total += start.elapsed_time(stop)
+            prev = None
+            for p, name in enumerate(moe.PHASES):
+                if name in ("fwd_begin", "bwd_begin"):
+                    prev = p
+                    continue
+                pms[name] += ev.elapsed(prev, p)
                 prev = p
-                continue
-            phase_ms[name] += ev.elapsed(prev, p)
-            prev = p
+        return total / n, {k: v / n for k, v in pms.items()}
+
+    # the timed region: the library's default schedule (backward branch on a second stream)
+    ms, phase_ms_timed = timed(args.steps)
+    log(f"[bench] {args.steps} steps, {ms:.3f} ms/step")
+    # per-phase breakdown: the same step with every kernel in launch order on one stream
+    layer.cfg.flags |= moe.MOE_F_SERIAL_BWD
+    n_serial = min(args.steps, 3)
+    ms_serial, phase_ms = timed(n_serial)
+    layer.cfg.flags &= ~moe.MOE_F_SERIAL_BWD
     torch.cuda.synchronize()
     moe.moe_set_phase_events(None, 0)
+    log(f"[bench] {n_serial} steps in launch order (phase breakdown), {ms_serial:.3f} ms/step")
     code = moe.moe_device_status(layer.workspace)
     if code != 0:
         log(f"[bench] device status {code}")
         return 1
-    ms = total_ms / args.steps
-    for k in phase_ms:
-        phase_ms[k] /= args.steps
-    log(f"[bench] {args.steps} steps, {ms:.3f} ms/step")
 
     tok_off = layer.saved_tensor("tok_off").cpu().numpy()
     work = phase_work(cfg, int(tok_off[-1]))
@@ -291,7 +300,11 @@ def main() -> int:
                          "roofline_frac": round(max(f / MXFP8_PEAK, b / HBM_PEAK) / (t * 1e-3), 4)}
     dom = max((p for p in phases), key=lambda p: phases[p]["ms"]) if args.dominant == "auto" else args.dominant
     f, b = work[dom]
-    t = phase_ms[dom] * 1e-3
+    # phases whose interval in the timed region covers that phase alone (the others overlap the
+    # backward's second-stream branch there): take those from the timed region itself
+    clean = dom in ("quant_x", "router", "topk", "schedule", "gateup", "down", "combine", "quant_dy",
+                    "wgrad_gateup")
+    t = (phase_ms_timed[dom] if clean else phase_ms[dom]) * 1e-3
     if f / MXFP8_PEAK >= b / HBM_PEAK:
         roof = {"bound": "mfma", "achieved": round(f / t / 1e12, 2), "peak": MXFP8_PEAK / 1e12, "unit": "TFLOP/s"}
     else:
@@ -299,6 +312,7 @@ def main() -> int:
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = measured_traffic(dom, ring=bool(args.flags & 2))
     roof["kernel"] = dom
+    roof["timed_in"] = "timed region" if clean else "launch-order pass"
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -326,6 +340,7 @@ def main() -> int:
         "mfma_frac_layer": round(flops_gemm / (ms * 1e-3) / MXFP8_PEAK, 4),
         "mfma_frac_gemms": round(flops_gemm / (gemm_ms * 1e-3) / MXFP8_PEAK, 4),
         "fwd_tflop": round(flops_fwd / 1e12, 3),
+        "ms_per_step_launch_order": round(ms_serial, 4),
         "phases": phases,
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -75,6 +75,15 @@ typedef struct moe_config {
 #define MOE_F_DIRECT_GATHER 1u
 #define MOE_F_RING_DISPATCH 2u
 
+/* Backward schedule.  By default moe_bwd runs the branch that needs only the forward's saved
+ * rows and dy (token-axis requantisation of X, H and w*dY, then dW2) on a second stream of the
+ * device, created by the library on first use with default priority and kept until the process
+ * ends, beside the router backward and the dgrad chain; the caller's stream waits for it before
+ * dW1, so the call stays ordered on the caller's stream as a whole.  MOE_F_SERIAL_BWD runs every
+ * kernel in launch order on the caller's stream instead (phase timing then covers every phase;
+ * results are identical either way). */
+#define MOE_F_SERIAL_BWD 4u
+
 /* Byte offsets inside the caller-owned `saved` buffer that moe_fwd fills and moe_bwd reads
  * (the schedule is built once and reused by the backward pass).  R = T*k routed rows,
  * RS = R + n_shared*T rows in expert-major ("permuted") order, S = n_shared, NX = E + S. */
@@ -152,7 +161,11 @@ moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const v
 /* Phase timing, for measurement only.  Phases of moe_fwd / moe_bwd, in launch order; the
  * library records events[p] on the call's stream right after phase p has been enqueued (and
  * events[MOE_PH_FWD_BEGIN] / events[MOE_PH_BWD_BEGIN] before the first launch), so the time
- * of phase p is the elapsed time between the previous recorded event and events[p].  The
+ * of phase p is the elapsed time between the previous recorded event and events[p].  Without
+ * MOE_F_SERIAL_BWD the phases of the second-stream branch (MOE_PH_TOKEN_REQUANT's X / H / dY
+ * part, MOE_PH_WGRAD_DOWN) overlap the others and their intervals do not measure them alone;
+ * events[MOE_PH_WGRAD_DOWN] is then recorded after the join, so MOE_PH_WGRAD_GATEUP still
+ * times dW1 alone.  The
  * caller creates the events (hipEventCreate) and keeps them alive; n_events = 0 turns timing
  * off.  Results are unaffected. */
 enum {

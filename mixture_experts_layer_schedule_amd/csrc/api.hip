@@ -48,7 +48,7 @@ moe_status check_config(const moe_config* c) {
   if (c->ring_rows < 0 || c->producer_wgs < 0 || c->producer_wgs > 128) return MOE_ESHAPE;
   if (c->ring_rows && (c->ring_rows < kChunkRows || c->ring_rows % kChunkRows)) return MOE_ESHAPE;
   if (c->chunk_rows != 0 && c->chunk_rows != kChunkRows) return MOE_ESHAPE;
-  if (c->flags & ~(MOE_F_DIRECT_GATHER | MOE_F_RING_DISPATCH)) return MOE_EINVAL;
+  if (c->flags & ~(MOE_F_DIRECT_GATHER | MOE_F_RING_DISPATCH | MOE_F_SERIAL_BWD)) return MOE_EINVAL;
   if ((c->flags & MOE_F_DIRECT_GATHER) && (c->flags & MOE_F_RING_DISPATCH)) return MOE_EINVAL;
   if (c->flags & MOE_F_RING_DISPATCH) return MOE_EINVAL;  // disabled: see the ring kernel's header
   if ((int64_t)c->T * c->k + (int64_t)c->n_shared * c->T >= (1ll << 30)) return MOE_ESHAPE;
@@ -146,6 +146,31 @@ moe_status ensure_init() {
     if (g_init_err == hipSuccess) g_init_err = ring_init();
   });
   return g_init_err == hipSuccess ? MOE_OK : MOE_ELAUNCH;
+}
+
+// Second stream of each device for the backward's independent branch (created on first use,
+// default priority, kept until the process ends) and the fork / join events around it.
+struct SideStream {
+  hipStream_t st = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool ok = false, tried = false;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+std::mutex g_side_mu;
+
+SideStream* side_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  SideStream& s = g_side[dev];
+  if (!s.tried) {
+    s.tried = true;
+    s.ok = hipStreamCreateWithFlags(&s.st, hipStreamNonBlocking) == hipSuccess &&
+           hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) == hipSuccess &&
+           hipEventCreateWithFlags(&s.join, hipEventDisableTiming) == hipSuccess;
+  }
+  return s.ok ? &s : nullptr;
 }
 
 #define MOE_TRY(expr)                      \
@@ -335,6 +360,51 @@ moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const v
   mark(stream, MOE_PH_BWD_BEGIN);
   MOE_TRY(launch_quant_rows(dy, 0, m.T, m.d, dyq, dys, stream));
   mark(stream, MOE_PH_QUANT_DY);
+
+  // Token-axis requantisation of the weight-gradient operands, and dW2[e] [d, I] = dYw^T H, depend
+  // only on the forward's saved rows and on dy: they run on the device's second stream, beside
+  // the router backward and the dgrad chain (whose buffers they do not touch), and are joined
+  // before dW1.  MOE_F_SERIAL_BWD (or no second stream) keeps everything in launch order.
+  SideStream* side = (cfg->flags & MOE_F_SERIAL_BWD) ? nullptr : side_stream();
+  hipStream_t sst = side ? side->st : stream;
+  TokArgs ta;
+  ta.s = sv;
+  ta.w = w;
+  ta.tok_off = tok_off;
+  ta.tile64 = tile64;
+  ta.ld = m.ld_tok;
+  const int tb = (int)m.tile64_bound;
+  WgradArgs wa;
+  wa.tok_off = tok_off;
+  wa.ld = m.ld_tok;
+  auto side_branch = [&]() -> moe_status {
+    ta.q = at<uint8_t>(saved, sl.xq); ta.qs = at<uint8_t>(saved, sl.xs); ta.cols = d; ta.src = TOK_X;
+    ta.out = at<uint8_t>(workspace, wl.xt); ta.outs = at<uint8_t>(workspace, wl.xts);
+    MOE_TRY(launch_token_requant(ta, tb, sst));
+    ta.q = at<uint8_t>(saved, sl.hq); ta.qs = at<uint8_t>(saved, sl.hs); ta.cols = I; ta.src = TOK_H;
+    ta.out = at<uint8_t>(workspace, wl.ht); ta.outs = at<uint8_t>(workspace, wl.hts);
+    MOE_TRY(launch_token_requant(ta, tb, sst));
+    ta.q = dyq; ta.qs = dys; ta.cols = d; ta.src = TOK_DYW;
+    ta.out = at<uint8_t>(workspace, wl.dyt); ta.outs = at<uint8_t>(workspace, wl.dyts);
+    MOE_TRY(launch_token_requant(ta, tb, sst));
+    return MOE_OK;
+  };
+  auto wgrad_down = [&]() -> moe_status {
+    WgradArgs a2 = wa;
+    a2.at = at<uint8_t>(workspace, wl.dyt); a2.ats = at<uint8_t>(workspace, wl.dyts);
+    a2.bt = at<uint8_t>(workspace, wl.ht); a2.bts = at<uint8_t>(workspace, wl.hts);
+    a2.dw = dw2; a2.M = d; a2.N = I; a2.n_exp = (int)m.NX;
+    MOE_TRY(launch_gemm_wgrad(a2, sst));
+    return MOE_OK;
+  };
+  if (side) {
+    MOE_TRY(hipEventRecord(side->fork, stream));
+    MOE_TRY(hipStreamWaitEvent(side->st, side->fork, 0));
+    if ((st = side_branch()) != MOE_OK) return st;
+    if ((st = wgrad_down()) != MOE_OK) return st;
+    MOE_TRY(hipEventRecord(side->join, side->st));
+  }
+
   MOE_TRY(launch_router_bwd((const uint16_t*)dy, at<float>(saved, sl.yslot), at<float>(saved, sl.logits), idx, w,
                             (int)m.T, (int)m.E, (int)m.k, (int)m.S, d, cfg->score_fn, dwv, dl, stream));
   mark(stream, MOE_PH_ROUTER_BWD);
@@ -376,36 +446,13 @@ moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const v
                            (uint16_t*)dx_bf16, dx_f32, stream));
   mark(stream, MOE_PH_DX_REDUCE);
 
-  // token-axis requantisation of the weight-gradient operands
-  TokArgs ta;
-  ta.s = sv;
-  ta.w = w;
-  ta.tok_off = tok_off;
-  ta.tile64 = tile64;
-  ta.ld = m.ld_tok;
-  const int tb = (int)m.tile64_bound;
-  ta.q = at<uint8_t>(saved, sl.xq); ta.qs = at<uint8_t>(saved, sl.xs); ta.cols = d; ta.src = TOK_X;
-  ta.out = at<uint8_t>(workspace, wl.xt); ta.outs = at<uint8_t>(workspace, wl.xts);
-  MOE_TRY(launch_token_requant(ta, tb, stream));
-  ta.q = at<uint8_t>(saved, sl.hq); ta.qs = at<uint8_t>(saved, sl.hs); ta.cols = I; ta.src = TOK_H;
-  ta.out = at<uint8_t>(workspace, wl.ht); ta.outs = at<uint8_t>(workspace, wl.hts);
-  MOE_TRY(launch_token_requant(ta, tb, stream));
-  ta.q = dyq; ta.qs = dys; ta.cols = d; ta.src = TOK_DYW;
-  ta.out = at<uint8_t>(workspace, wl.dyt); ta.outs = at<uint8_t>(workspace, wl.dyts);
-  MOE_TRY(launch_token_requant(ta, tb, stream));
+  if (!side && (st = side_branch()) != MOE_OK) return st;
   ta.q = dd.dguq; ta.qs = dd.dgus; ta.cols = 2 * I; ta.src = TOK_DGU;
   ta.out = at<uint8_t>(workspace, wl.dgut); ta.outs = at<uint8_t>(workspace, wl.dguts);
   MOE_TRY(launch_token_requant(ta, tb, stream));
-
   mark(stream, MOE_PH_TOKEN_REQUANT);
-  WgradArgs wa;
-  wa.tok_off = tok_off;
-  wa.ld = m.ld_tok;
-  // dW2[e] [d, I] = dYw^T H
-  wa.at = at<uint8_t>(workspace, wl.dyt); wa.ats = at<uint8_t>(workspace, wl.dyts);
-  wa.bt = at<uint8_t>(workspace, wl.ht); wa.bts = at<uint8_t>(workspace, wl.hts);
-  wa.dw = dw2; wa.M = d; wa.N = I; wa.n_exp = (int)m.NX;
-  MOE_TRY(launch_gemm_wgrad(wa, stream));
+  if (!side && (st = wgrad_down()) != MOE_OK) return st;
+  if (side) MOE_TRY(hipStreamWaitEvent(stream, side->join, 0));
   mark(stream, MOE_PH_WGRAD_DOWN);
   // dW1[e] [2I, d] = dGU^T X
   wa.at = at<uint8_t>(workspace, wl.dgut); wa.ats = at<uint8_t>(workspace, wl.dguts);

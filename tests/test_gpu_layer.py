@@ -168,3 +168,25 @@ def test_bitwise_reproducible(pair):
     assert torch.equal(y0, layer.y32)
     assert torch.equal(dx0, layer.dx32)
     assert torch.equal(dw10, layer.dw1)
+
+
+def test_serial_and_concurrent_backward_identical(pair):
+    """The backward's second-stream schedule (default) and the launch-order schedule
+    (MOE_F_SERIAL_BWD) produce bitwise identical gradients."""
+    cfg, inp, fw, bw, layer = pair
+    import torch
+    import mixture_experts_layer_schedule_amd as moe
+    layer.forward()
+    layer.backward()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (layer.dx32, layer.dw1, layer.dw2, layer.dw_r)]
+    layer.cfg.flags |= moe.MOE_F_SERIAL_BWD
+    try:
+        for t in (layer.dx32, layer.dw1, layer.dw2, layer.dw_r):
+            t.zero_()
+        layer.backward()
+        torch.cuda.synchronize()
+    finally:
+        layer.cfg.flags &= ~moe.MOE_F_SERIAL_BWD
+    for name, a, b in zip(("dx", "dW1", "dW2", "dW_r"), ref, (layer.dx32, layer.dw1, layer.dw2, layer.dw_r)):
+        assert torch.equal(a, b), name

@@ -62,6 +62,13 @@ def test_query_rejects_bad_config(kw, status):
     assert ei.value.status == status
 
 
+@pytest.mark.parametrize("flags", [0, 1, 4, 5])
+def test_query_accepts_schedule_flags(flags):
+    """Direct gather (1) and the launch-order backward (4) are valid alone and together."""
+    ws, _ = moe.moe_query(moe.make_config(256, 256, 8, 2, 128, flags=flags))
+    assert ws > 0
+
+
 def test_forward_rejects_null_and_misaligned_pointers_without_launching():
     cfg = moe.make_config(256, 256, 8, 2, 128)
     with pytest.raises(moe.MoeError) as ei:
