@@ -88,7 +88,8 @@ PHASE_DISPATCHES = {  # phase -> kernel dispatches of one step (name#index in la
     "gateup": ["k_gemm_gateup#0"], "down": ["k_gemm_down#0"], "combine": ["k_combine#0"],
     "router_bwd": ["k_router_bwd#0"],
     "dgrad_down": ["k_gemm_dgrad_down#0"], "dgrad_gateup": ["k_gemm_dgrad_gateup#0"],
-    "dx_reduce": ["k_dx_reduce#0"], "wgrad_down": ["k_gemm_wgrad#0"], "wgrad_gateup": ["k_gemm_wgrad#1"],
+    "dx_reduce": ["k_dx_reduce#0"], "wgrad_down": ["k_gemm_wgrad<8, 0>#0"],
+    "wgrad_gateup": ["k_gemm_wgrad<8, 1>#0"],
 }
 
 
@@ -120,8 +121,8 @@ def measured_traffic(phase: str, ring: bool):
     table = {}
     for line in text:
         parts = line.split()
-        if len(parts) == 4 and not line.startswith("#"):
-            table[parts[0]] = float(parts[2]) + float(parts[3])
+        if len(parts) >= 4 and not line.startswith("#"):  # name (may hold spaces), n, fetch GB, write GB
+            table[" ".join(parts[:-3])] = float(parts[-2]) + float(parts[-1])
     keys = PHASE_DISPATCHES.get(phase)
     if keys and ring and phase == "gateup":
         keys = ["k_ring_gateup#0"]

@@ -394,7 +394,7 @@ moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const v
     a2.at = at<uint8_t>(workspace, wl.dyt); a2.ats = at<uint8_t>(workspace, wl.dyts);
     a2.bt = at<uint8_t>(workspace, wl.ht); a2.bts = at<uint8_t>(workspace, wl.hts);
     a2.dw = dw2; a2.M = d; a2.N = I; a2.n_exp = (int)m.NX;
-    MOE_TRY(launch_gemm_wgrad(a2, sst));
+    MOE_TRY(launch_gemm_wgrad(a2, 0, sst));
     return MOE_OK;
   };
   if (side) {
@@ -458,7 +458,7 @@ moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const v
   wa.at = at<uint8_t>(workspace, wl.dgut); wa.ats = at<uint8_t>(workspace, wl.dguts);
   wa.bt = at<uint8_t>(workspace, wl.xt); wa.bts = at<uint8_t>(workspace, wl.xts);
   wa.dw = dw1; wa.M = 2 * I; wa.N = d; wa.n_exp = (int)m.NX;
-  MOE_TRY(launch_gemm_wgrad(wa, stream));
+  MOE_TRY(launch_gemm_wgrad(wa, 1, stream));
   mark(stream, MOE_PH_WGRAD_GATEUP);
   return MOE_OK;
 }

@@ -235,7 +235,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_gateup(DgradGateUpArgs p)
 // offset.  An expert with no tokens writes zeros.  Tiles are 256 x 256 (128 x 256 when M is not
 // a multiple of 256): the token count is short, so a bigger tile amortises each load latency.
 
-template <int kWgradF>
+// kWhich only names the launch (0: dW2, 1: dW1) so that traces tell the two GEMMs apart.
+template <int kWgradF, int kWhich>
 __global__ __launch_bounds__(256, 1) void k_gemm_wgrad(WgradArgs p) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int MT = p.M / (32 * kWgradF), NT = (p.N + TN - 1) / TN;
@@ -299,18 +300,23 @@ hipError_t launch_gemm_dgrad_gateup(const DgradGateUpArgs& a, int tiles_bound, h
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_wgrad(const WgradArgs& a, hipStream_t st) {
+template <int kWhich>
+static hipError_t launch_wgrad(const WgradArgs& a, hipStream_t st) {
   // 256-row tiles when M allows (half the workgroups, each with twice the work per load latency)
   if (a.M % 256 == 0) {
     const int blocks = a.n_exp * (a.M / 256) * ((a.N + TN - 1) / TN);
-    hipLaunchKernelGGL(k_gemm_wgrad<8>, dim3(blocks), dim3(256), wgrad_lds_bytes(), st, a);
+    hipLaunchKernelGGL((k_gemm_wgrad<8, kWhich>), dim3(blocks), dim3(256), wgrad_lds_bytes(), st, a);
   } else if (a.M % 128 == 0) {
     const int blocks = a.n_exp * (a.M / 128) * ((a.N + TN - 1) / TN);
-    hipLaunchKernelGGL(k_gemm_wgrad<4>, dim3(blocks), dim3(256), wgrad_lds_bytes(), st, a);
+    hipLaunchKernelGGL((k_gemm_wgrad<4, kWhich>), dim3(blocks), dim3(256), wgrad_lds_bytes(), st, a);
   } else {
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_wgrad(const WgradArgs& a, int which, hipStream_t st) {
+  return which ? launch_wgrad<1>(a, st) : launch_wgrad<0>(a, st);
 }
 
 hipError_t gemm_init() {
@@ -320,12 +326,9 @@ hipError_t gemm_init() {
   if ((e = hipFuncSetAttribute((const void*)k_gemm_down, hipFuncAttributeMaxDynamicSharedMemorySize, bytes))) return e;
   if ((e = hipFuncSetAttribute((const void*)k_gemm_dgrad_down, hipFuncAttributeMaxDynamicSharedMemorySize, bytes))) return e;
   if ((e = hipFuncSetAttribute((const void*)k_gemm_dgrad_gateup, hipFuncAttributeMaxDynamicSharedMemorySize, bytes))) return e;
-  if ((e = hipFuncSetAttribute((const void*)k_gemm_wgrad<8>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)wgrad_lds_bytes())))
-    return e;
-  if ((e = hipFuncSetAttribute((const void*)k_gemm_wgrad<4>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)wgrad_lds_bytes())))
-    return e;
+  for (const void* k : {(const void*)k_gemm_wgrad<8, 0>, (const void*)k_gemm_wgrad<8, 1>,
+                        (const void*)k_gemm_wgrad<4, 0>, (const void*)k_gemm_wgrad<4, 1>})
+    if ((e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)wgrad_lds_bytes()))) return e;
   return hipSuccess;
 }
 

@@ -79,7 +79,8 @@ hipError_t launch_gemm_gateup(const GateUpArgs&, int tiles_bound, hipStream_t);
 hipError_t launch_gemm_down(const DownArgs&, int tiles_bound, hipStream_t);
 hipError_t launch_gemm_dgrad_down(const DgradDownArgs&, int tiles_bound, hipStream_t);
 hipError_t launch_gemm_dgrad_gateup(const DgradGateUpArgs&, int tiles_bound, hipStream_t);
-hipError_t launch_gemm_wgrad(const WgradArgs&, hipStream_t);
+// which: 0 for dW2, 1 for dW1 (separate kernel names in traces)
+hipError_t launch_gemm_wgrad(const WgradArgs&, int which, hipStream_t);
 
 // MXFP8 quantisation along the contiguous axis of a [rows, cols] bf16 (src_f32 = 0) or
 // float32 (src_f32 = 1) matrix.
