@@ -40,8 +40,11 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ yslot
 }
 
 // Per token: dw[t, j] = <dy[t], Yslot[t, j]> (reverse-combine of the weights), then the
-// gradient of the selected logits.  One 256-thread workgroup per token; sums reduce in a fixed
-// tree.
+// gradient of the selected logits.  One 256-thread workgroup per token: thread i holds dy at
+// columns 4(i + 256m) in registers and reads each slot row with 16-byte loads, so a token's
+// k + 1 rows stream at full width; the partial sums reduce in a fixed tree.
+constexpr int kRbQuads = 8;  // column quads per thread and pass (d <= 8192 in one pass)
+
 __global__ __launch_bounds__(256) void k_router_bwd(const uint16_t* __restrict__ dy, const float* __restrict__ yslot,
                                                     const float* __restrict__ L, const int32_t* __restrict__ idx,
                                                     const float* __restrict__ w, int E, int k, int S, int d, int score,
@@ -50,16 +53,43 @@ __global__ __launch_bounds__(256) void k_router_bwd(const uint16_t* __restrict__
   __shared__ float dws[16];
   const int t = blockIdx.x;
   const int wave = threadIdx.x >> 6;
+  const int nq = d / 4;
   const uint16_t* dyr = dy + (size_t)t * d;
-  for (int j = 0; j < k; ++j) {
-    const float* yr = yslot + ((size_t)t * (k + S) + j) * d;
-    float acc = 0.0f;
-    for (int c = threadIdx.x; c < d; c += 256) acc += bf16_to_f32(dyr[c]) * yr[c];
-    acc = group_sum<64>(acc);
-    if (lane_id() == 0) part[j][wave] = acc;
+  const float* ys = yslot + (size_t)t * (k + S) * d;
+  float acc[16];
+  static_for<16>([&]<int j>() { acc[j] = 0.0f; });
+  for (int q0 = 0; q0 < nq; q0 += 256 * kRbQuads) {
+    v4f dv[kRbQuads];
+    static_for<kRbQuads>([&]<int m>() {
+      const int q = q0 + (int)threadIdx.x + 256 * m;
+      dv[m] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+      if (q < nq) {
+        const v2i b = *(const v2i*)(dyr + 4 * q);
+        dv[m] = (v4f){__uint_as_float((uint32_t)b[0] << 16), __uint_as_float((uint32_t)b[0] & 0xFFFF0000u),
+                      __uint_as_float((uint32_t)b[1] << 16), __uint_as_float((uint32_t)b[1] & 0xFFFF0000u)};
+      }
+    });
+    static_for<16>([&]<int j>() {
+      if (j < k) {
+        v4f y[kRbQuads];
+        static_for<kRbQuads>([&]<int m>() {
+          const int q = q0 + (int)threadIdx.x + 256 * m;
+          y[m] = q < nq ? *(const v4f*)(ys + (size_t)j * d + 4 * q) : (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+        });
+        static_for<kRbQuads>([&]<int m>() {
+          acc[j] += dv[m][0] * y[m][0] + dv[m][1] * y[m][1] + dv[m][2] * y[m][2] + dv[m][3] * y[m][3];
+        });
+      }
+    });
   }
+  static_for<16>([&]<int j>() {
+    if (j < k) {
+      const float v = group_sum<64>(acc[j]);
+      if (lane_id() == 0) part[j][wave] = v;
+    }
+  });
   __syncthreads();
-  if (threadIdx.x < k) {
+  if ((int)threadIdx.x < k) {
     int j = threadIdx.x;
     dws[j] = (part[j][0] + part[j][1]) + (part[j][2] + part[j][3]);
   }
@@ -84,17 +114,26 @@ __global__ __launch_bounds__(256) void k_router_bwd(const uint16_t* __restrict__
   }
 }
 
-// dW_r[e, n] = sum over the expert's routed rows (increasing token order) of dL * x[t, n].
+// dW_r[e, n] = sum over the expert's routed rows (increasing token order) of dL * x[t, n].  The
+// rows' indices and values are loaded 8 at a time ahead of the (in-order) accumulation.
 __global__ __launch_bounds__(256) void k_router_wgrad(SchedView s, const float* __restrict__ dl,
                                                       const uint16_t* __restrict__ x, int d, float* __restrict__ dwr) {
   const int e = blockIdx.y;
   const int n = blockIdx.x * 256 + threadIdx.x;
   if (n >= d) return;
   float acc = 0.0f;
-  const int r1 = s.offsets[e + 1];
-  for (int r = s.offsets[e]; r < r1; ++r) {
-    int sid = s.perm[r];
-    acc += dl[sid] * bf16_to_f32(x[(size_t)(sid / s.k) * d + n]);
+  const int r0 = s.offsets[e], r1 = s.offsets[e + 1];
+  for (int r = r0; r < r1; r += 8) {
+    int sid[8];
+    float dv[8], xv[8];
+    static_for<8>([&]<int u>() { sid[u] = r + u < r1 ? s.perm[r + u] : s.perm[r]; });
+    static_for<8>([&]<int u>() {
+      dv[u] = dl[sid[u]];
+      xv[u] = bf16_to_f32(x[(size_t)(sid[u] / s.k) * d + n]);
+    });
+    static_for<8>([&]<int u>() {
+      if (r + u < r1) acc += dv[u] * xv[u];
+    });
   }
   dwr[(size_t)e * d + n] = acc;
 }
