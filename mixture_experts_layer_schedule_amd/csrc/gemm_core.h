@@ -253,11 +253,14 @@ MOE_DEV void compute_stage(const uint8_t* st, v16f (&acc)[F][2], const Hook& hoo
       });
       // independent vector work placed here issues while the matrix core runs the group
       if constexpr (!Hook::kEmpty) {
-        static_for<2>([&]<int j>() {  // the group's products exist before the hook's code
-          constexpr int mi = 2 * g + j;
-          if constexpr (mi < F) pin_agprs(acc[mi][0], acc[mi][1]);
-        });
         hook.template operator()<kk * NG + g, 2 * NG>();
+        // interleave: one matrix instruction, then a share of the hook's vector work, so the
+        // vector work issues while the matrix core runs
+        constexpr int NM = 2 * ((2 * g + 1 < F) ? 2 : 1);
+        static_for<NM>([&]<int x>() {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 28, 0);
+        });
       }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -423,7 +426,9 @@ MOE_DEV void mainloop_tb(uint8_t* lds, const TileLoads<F>& L, TransB& tb, int nk
     // (in the last stage this requantises stale registers into the B region of the free buffer,
     // which nothing reads afterwards: cheaper than a branch)
     compute_stage<F>(lds + (t % 2) * STAGE_BYTES, acc, RequantHook{tb, lds + ((t + 1) % 2) * STAGE_BYTES});
-    if (t + 2 < nk) tb.advance();
+    // unconditional (past the last load it copies stale registers that nothing uses): a branch
+    // after the matrix instructions would let the compiler sink them below the vector work
+    tb.advance();
   }
 }
 
