@@ -62,8 +62,12 @@ MOE_DEV float clamp448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
 
 // Four already-scaled values -> four e4m3 codes (round to nearest even) in one word.
 // The conversion instruction does not saturate, so values are clamped first.
+// The first conversion writes the low half of its destination and keeps the high half, which
+// the second one overwrites: any value serves as the first's "old" word, so the clamped input
+// itself is passed (no register has to be zeroed).
 MOE_DEV uint32_t pack4_e4m3(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
+  const float ca = clamp448(a);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(ca, clamp448(b), __float_as_int(ca), false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), w, true);
   return (uint32_t)w;
 }
@@ -95,12 +99,16 @@ MOE_DEV float group_max(float v) {  // max over aligned groups of W lanes (W pow
 // 2 and 1 (DPP) leave every lane of a 16-lane row with the row maximum, then v_permlane16_swap
 // exchanges the maxima of the two rows of each 32-lane half.
 MOE_DEV float group_max32(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false)));
-  const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
-  return fmaxf(__int_as_float(pr[0]), __int_as_float(pr[1]));
+  // v >= 0: non-negative floats order like their bit patterns, so the maximum is taken on the
+  // integers (a float maximum of values that crossed lanes as integers is preceded by a
+  // canonicalising instruction each time)
+  uint32_t u = __float_as_uint(v);
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x128, 0xF, 0xF, false));
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x124, 0xF, 0xF, false));
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x122, 0xF, 0xF, false));
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x121, 0xF, 0xF, false));
+  const auto pr = __builtin_amdgcn_permlane16_swap((int)u, (int)u, false, false);
+  return __uint_as_float(max((uint32_t)pr[0], (uint32_t)pr[1]));
 }
 
 template <int W>

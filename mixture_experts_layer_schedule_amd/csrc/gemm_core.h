@@ -339,7 +339,9 @@ struct TransB {
     static_for<8>([&]<int j>() { nsraw[j] = s[soff + (r0 + j) * (uint32_t)(N / 32)]; });
   }
 
-  // The in-flight stage becomes the one to requantise (waits for its loads).
+  // The in-flight stage becomes the one to requantise (waits for its loads).  (Two register
+  // sets alternating by stage parity would save these copies, but the two-stage loop body that
+  // needs makes the kernel spill.)
   MOE_DEV void advance() {
     static_for<8>([&]<int j>() {
       raw[j] = nraw[j];
@@ -362,12 +364,14 @@ struct TransB {
     static_for<2>([&]<int c>() {
       float m = 0.0f;
       static_for<8>([&]<int j>() { m = fmaxf(m, fabsf(v[j][c])); });
-      // maximum over the lanes l ^ 16, l ^ 32, l ^ 48 (the other 24 rows of the block)
-      const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_int(m), __float_as_int(m), false, false);
-      m = fmaxf(__int_as_float(p16[0]), __int_as_float(p16[1]));
-      const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_int(m), __float_as_int(m), false, false);
-      m = fmaxf(__int_as_float(p32[0]), __int_as_float(p32[1]));
-      const uint32_t byte = e8m0_from_amax(m);
+      // maximum over the lanes l ^ 16, l ^ 32, l ^ 48 (the other 24 rows of the block); the
+      // maxima are non-negative, so they are compared as integers (no canonicalisation)
+      uint32_t mu = __float_as_uint(m);
+      const auto p16 = __builtin_amdgcn_permlane16_swap((int)mu, (int)mu, false, false);
+      mu = max((uint32_t)p16[0], (uint32_t)p16[1]);
+      const auto p32 = __builtin_amdgcn_permlane32_swap((int)mu, (int)mu, false, false);
+      mu = max((uint32_t)p32[0], (uint32_t)p32[1]);
+      const uint32_t byte = e8m0_from_amax(__uint_as_float(mu));
       const float inv = e8m0_inv_scale(byte);
       v2i codes;
       codes[0] = (int)pack4_e4m3(v[0][c] * inv, v[1][c] * inv, v[2][c] * inv, v[3][c] * inv);
@@ -439,7 +443,7 @@ MOE_DEV uint32_t quant_lane32(float v, uint32_t* scale) {
   uint32_t byte = e8m0_from_amax(amax);
   *scale = byte;
   float x = clamp448(v * e8m0_inv_scale(byte));
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.0f, 0, false) & 0xFFu;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.0f, __float_as_int(x), false) & 0xFFu;
 }
 
 // silu(g) = g * sigmoid(g) with the hardware reciprocal (1 ulp).
