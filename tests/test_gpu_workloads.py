@@ -1,0 +1,167 @@
+"""Full-size forward parity for the other workloads: the Qwen3-30B-A3B-like layer (T=2048, d=2048,
+128 experts, top-8 softmax, I=768, seed 1), the DeepSeek-V3 layer forward (T=8192, d=7168, 256
+experts, top-8 sigmoid-normalised, I=2048, seed 2) and the Kimi-K2-shaped skewed layer (T=16384,
+d=7168, 384 routed experts + 1 shared, top-8 sigmoid-normalised with a Zipf router bias, I=2048,
+seed 3), each run on the GPU exactly as bench.py runs a layer.
+
+The oracle cannot run these layers whole in a test's time, so it checks what it can compute
+piece by piece on the same seeded inputs:
+
+* routing of every token and the whole schedule, bit-exact (a differing selection is allowed only
+  for a near-tie that float32 logits cannot order, and none is expected);
+* x quantisation, bit-exact;
+* the median-load and the maximum-load routed expert (and the shared expert), on up to 384 of
+  their rows (an expert's rows are independent in the forward pass): G/U within the accumulation
+  model, H codes unique-or-admissible, their Y slot rows within 1e-2 RMS + envelope;
+* one sampled token end to end (all its experts): y within 1e-2 RMS + envelope.
+"""
+import numpy as np
+import pytest
+
+import moe_inputs
+import oracle
+from oracle import envelope
+from oracle.layer import _qdq
+from helpers import log, rms, to_np
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+EPS = 2.0 ** -15
+MAX_ROWS = 384
+WORKLOADS = ["qwen3_30b_a3b", "dsv3_fwd", "kimi_k2_skew"]
+
+
+@pytest.fixture(scope="module", params=WORKLOADS)
+def run(request):
+    import torch
+    from mixture_experts_layer_schedule_amd import MoeLayer
+    import mixture_experts_layer_schedule_amd as moe
+
+    cfg = moe_inputs.CONFIGS[request.param]
+    log(f"{cfg.name}: inputs and {cfg.E + cfg.n_shared} experts")
+    inp = moe_inputs.layer_inputs(cfg, with_dy=False)
+    layer = MoeLayer.from_config(cfg, with_backward=False)
+    layer.set_inputs(inp.x_bits, inp.w_r_bits, inp.bias, None)
+    layer.load_experts(moe_inputs.iter_expert_weights(cfg, threads=16))
+    log(f"{cfg.name}: forward")
+    layer.forward()
+    torch.cuda.synchronize()
+    assert moe.moe_device_status(layer.workspace) == 0
+    cache = {}
+
+    def experts(e):
+        if e not in cache:
+            log(f"{cfg.name}: oracle weights of expert {e}")
+            w1, w2 = moe_inputs.expert_weights(cfg, e)
+            cache[e] = (_qdq(w1, 1, True)[2], _qdq(w2, 1, True)[2])
+        return cache[e]
+
+    yield cfg, inp, layer, experts
+    del layer, cache
+    torch.cuda.empty_cache()
+
+
+def _check(name, got, ref, bound):
+    got = np.asarray(got, dtype=np.float64)
+    r = rms(ref)
+    err = np.abs(got - ref)
+    log(f"  {name}: max|err|/rms {err.max() / r:.3e}; beyond {TOL:g} rms: {int((err > TOL * r).sum())}; "
+        f"envelope max {bound.max() / r:.2e} mean {bound.mean() / r:.2e} rms")
+    assert np.all(err <= TOL * r + bound), name
+
+
+def test_routing_and_schedule(run):
+    cfg, inp, layer, experts = run
+    x = inp.x.astype(np.float64)
+    L = oracle.router_logits(x, inp.w_r, inp.bias)
+    idx = oracle.select_topk(L, cfg.k)
+    gidx = to_np(layer.saved_tensor("idx"))
+    diff = np.where(np.any(gidx != idx, axis=1))[0]
+    log(f"{cfg.name}: tokens whose selection differs from the oracle: {len(diff)}")
+    gL = to_np(layer.saved_tensor("logits")).astype(np.float64)
+    bound = 1e-5 * (np.abs(x) @ np.abs(inp.w_r.astype(np.float64)).T + (0 if inp.bias is None else np.abs(inp.bias)))
+    assert np.all(np.abs(gL - L) <= bound)
+    for t in diff:  # a differing selection must be a near-tie the float32 logits cannot order
+        s = np.sort(L[t])[::-1]
+        assert s[cfg.k - 1] - s[cfg.k] <= 2 * bound[t].max(), t
+    NX = cfg.E + cfg.n_shared
+    counts = to_np(layer.saved_tensor("counts"))
+    if len(diff) == 0:
+        sched = oracle.build_schedule(idx, cfg.E)
+        assert np.array_equal(to_np(layer.saved_tensor("perm")), sched.perm)
+        assert np.array_equal(to_np(layer.saved_tensor("pos")), sched.pos)
+        assert np.array_equal(counts[:cfg.E], sched.counts)
+    assert np.all(counts[cfg.E:NX] == cfg.T)
+    assert np.array_equal(to_np(layer.saved_tensor("offsets")), np.concatenate([[0], np.cumsum(counts)]))
+    perm = to_np(layer.saved_tensor("perm"))
+    assert np.array_equal(np.sort(perm), np.arange(cfg.T * cfg.k))  # every routed row once: none dropped
+    assert np.array_equal(perm, oracle.build_schedule(gidx, cfg.E).perm)
+    log(f"{cfg.name}: rows per routed expert min {counts[:cfg.E].min()} mean {counts[:cfg.E].mean():.0f} "
+        f"max {counts[:cfg.E].max()}")
+    w = oracle.routing_weights(L, idx, cfg.score)
+    assert np.max(np.abs(to_np(layer.saved_tensor("w")) - w)) <= 1e-5
+
+
+def test_x_quantised_bit_exact(run):
+    cfg, inp, layer, experts = run
+    xq, xs = oracle.quantize(inp.x.astype(np.float64), axis=1)
+    assert np.array_equal(to_np(layer.saved_tensor("xq")), xq)
+    assert np.array_equal(to_np(layer.saved_tensor("xs")), xs)
+
+
+def test_sampled_experts(run):
+    cfg, inp, layer, experts = run
+    k, S = cfg.k, cfg.n_shared
+    R = cfg.T * k
+    counts = to_np(layer.saved_tensor("counts"))
+    offs = to_np(layer.saved_tensor("offsets"))
+    perm = to_np(layer.saved_tensor("perm"))
+    order = np.argsort(counts[:cfg.E], kind="stable")
+    picks = [int(order[len(order) // 2]), int(order[-1])] + list(range(cfg.E, cfg.E + S))
+    xq, xs = oracle.quantize(inp.x.astype(np.float64), axis=1)
+    X = oracle.dequantize(xq, xs, axis=1)
+    G, U = layer.saved_tensor("g"), layer.saved_tensor("u")
+    ys = layer.saved_tensor("yslot").view(-1, cfg.d)
+    rng = np.random.default_rng(0)
+    for e in picks:
+        lo, hi = int(offs[e]), int(offs[e + 1])
+        rows = np.arange(lo, hi)
+        if len(rows) > MAX_ROWS:  # rows are independent in the forward pass: check a sorted sample
+            rows = np.sort(rng.choice(rows, MAX_ROWS, replace=False))
+        if e < cfg.E:
+            toks = perm[rows] // k
+            slots = toks * (k + S) + perm[rows] % k
+        else:
+            toks = rows - R - (e - cfg.E) * cfg.T
+            slots = toks * (k + S) + k + (e - cfg.E)
+        W1, W2 = experts(e)
+        log(f"{cfg.name}: expert {e} ({hi - lo} rows, {len(rows)} checked)")
+        fe = oracle.expert_forward(X[toks], W1, W2)
+        eG, eU, Hlo, Hhi, devH, BY = envelope.expert_forward_envelope(fe, X[toks], W1, W2, EPS)
+        g = to_np(G[rows]).astype(np.float64)
+        u = to_np(U[rows]).astype(np.float64)
+        log(f"  G err / model max {np.max(np.abs(g - fe.G) / eG):.3f}")
+        assert np.all(np.abs(g - fe.G) <= eG) and np.all(np.abs(u - fe.U) <= eU)
+        H = oracle.dequantize(to_np(layer.saved_tensor("hq")[rows]), to_np(layer.saved_tensor("hs")[rows]), axis=1)
+        uniq = Hlo == Hhi
+        log(f"  H codes: {int((~uniq).sum())} of {uniq.size} have two admissible values")
+        assert np.all(H[uniq] == fe.H[uniq]) and np.all((H >= Hlo) & (H <= Hhi))
+        _check(f"Y slot rows of expert {e}", to_np(ys[slots]), fe.Y, BY)
+
+
+def test_sampled_token(run):
+    import torch
+
+    cfg, inp, layer, experts = run
+    t = cfg.T // 3 + 7
+    x = inp.x[t:t + 1].astype(np.float64)
+    log(f"{cfg.name}: token {t}: oracle forward")
+    fw = oracle.layer_forward(x, inp.w_r, experts, cfg.k, cfg.score, inp.bias, cfg.n_shared)
+    fenv = envelope.forward_envelope(fw, experts, EPS)
+    assert np.array_equal(to_np(layer.saved_tensor("idx")[t]), fw.idx[0])
+    _check(f"y[{t}]", to_np(layer.y32[t:t + 1]), fw.y, fenv.By)
+    # the bf16 output is the float32 one rounded to nearest even
+    y16 = to_np(layer.y[t:t + 1].view(torch.int16))
+    ref16 = torch.from_numpy(to_np(layer.y32[t:t + 1])).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(y16, ref16)
