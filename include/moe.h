@@ -84,6 +84,15 @@ typedef struct moe_config {
  * results are identical either way). */
 #define MOE_F_SERIAL_BWD 4u
 
+/* Check mode of the combine: every expert is replaced by the identity (the row of expert e for
+ * token t is x[t] itself), so moe_fwd runs the router, top-k, schedule and x quantisation, writes
+ * x into every (token, slot) row of the saved Y slots and then the ordinary fixed-order weighted
+ * combine.  The combine weights sum to 1 (knowledge card "Mixture-of-Kittens——面向NVL72的开源MoE
+ * 训练megakernel", 方法/产品要点: deterministic combine), so the bf16 output is x (times 1 + n_shared
+ * with shared experts) bit for bit.  The weight pointers are still required and are not read;
+ * moe_bwd rejects the flag with MOE_EINVAL (there is no saved expert state to differentiate). */
+#define MOE_F_IDENTITY_EXPERTS 8u
+
 /* Byte offsets inside the caller-owned `saved` buffer that moe_fwd fills and moe_bwd reads
  * (the schedule is built once and reused by the backward pass).  R = T*k routed rows,
  * RS = R + n_shared*T rows in expert-major ("permuted") order, S = n_shared, NX = E + S. */

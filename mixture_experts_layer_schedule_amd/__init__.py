@@ -18,6 +18,7 @@ MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_F_DIRECT_GATHER = 1
 MOE_F_RING_DISPATCH = 2
 MOE_F_SERIAL_BWD = 4
+MOE_F_IDENTITY_EXPERTS = 8
 
 # every symbol include/moe.h declares
 EXPORTS = ("moe_query", "moe_quantize_mxfp8", "moe_requant_transpose", "moe_fwd", "moe_bwd",

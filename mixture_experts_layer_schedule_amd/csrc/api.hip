@@ -48,7 +48,8 @@ moe_status check_config(const moe_config* c) {
   if (c->ring_rows < 0 || c->producer_wgs < 0 || c->producer_wgs > 128) return MOE_ESHAPE;
   if (c->ring_rows && (c->ring_rows < kChunkRows || c->ring_rows % kChunkRows)) return MOE_ESHAPE;
   if (c->chunk_rows != 0 && c->chunk_rows != kChunkRows) return MOE_ESHAPE;
-  if (c->flags & ~(MOE_F_DIRECT_GATHER | MOE_F_RING_DISPATCH | MOE_F_SERIAL_BWD)) return MOE_EINVAL;
+  if (c->flags & ~(MOE_F_DIRECT_GATHER | MOE_F_RING_DISPATCH | MOE_F_SERIAL_BWD | MOE_F_IDENTITY_EXPERTS))
+    return MOE_EINVAL;
   if ((c->flags & MOE_F_DIRECT_GATHER) && (c->flags & MOE_F_RING_DISPATCH)) return MOE_EINVAL;
   if (c->flags & MOE_F_RING_DISPATCH) return MOE_EINVAL;  // disabled: see the ring kernel's header
   if ((int64_t)c->T * c->k + (int64_t)c->n_shared * c->T >= (1ll << 30)) return MOE_ESHAPE;
@@ -269,6 +270,16 @@ moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, c
   MOE_TRY(launch_schedule(sb, stream));
   mark(stream, MOE_PH_SCHEDULE);
 
+  if (cfg->flags & MOE_F_IDENTITY_EXPERTS) {  // combine check: x in every slot row, then the combine
+    float* yslot = at<float>(saved, sl.yslot);
+    MOE_TRY(launch_identity_slots((const uint16_t*)x, (int)m.T, (int)(m.k + m.S), d, yslot, stream));
+    mark(stream, MOE_PH_GATEUP);
+    mark(stream, MOE_PH_DOWN);
+    MOE_TRY(launch_combine(yslot, w, (int)m.T, (int)m.k, (int)m.S, d, (uint16_t*)y_bf16, y_f32, stream));
+    mark(stream, MOE_PH_COMBINE);
+    return MOE_OK;
+  }
+
   const SchedView sv = sched_view(saved, sl, m);
   GateUpArgs ga;
   ga.s = sv;
@@ -335,6 +346,7 @@ moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const v
                    float* dx_f32, float* dw_router, float* dw1, float* dw2, void* workspace, hipStream_t stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
+  if (cfg->flags & MOE_F_IDENTITY_EXPERTS) return MOE_EINVAL;  // forward-only check mode
   if (!dy || !x || !w_router || !w1q || !w1s || !w2q || !w2s || !saved || !dx_bf16 || !dw_router || !dw1 || !dw2 ||
       !workspace)
     return MOE_EINVAL;

@@ -39,6 +39,26 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ yslot
   }
 }
 
+// Identity experts (a check of the dispatch-free combine path): every slot row of token t holds
+// x[t] widened to float32 (exact); 4 columns per thread.
+__global__ __launch_bounds__(256) void k_identity_slots(const uint16_t* __restrict__ x, int T, int slots, int d,
+                                                        float* __restrict__ yslot) {
+  const int64_t n4 = (int64_t)T * slots * (d / 4);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < n4; g += stride) {
+    const int64_t row = g / (d / 4);  // t * slots + j
+    const int64_t c = (g - row * (d / 4)) * 4;
+    const int64_t t = row / slots;
+    const v2i b = *(const v2i*)(x + t * d + c);
+    v4f y;
+    y[0] = __uint_as_float((uint32_t)b[0] << 16);
+    y[1] = __uint_as_float((uint32_t)b[0] & 0xFFFF0000u);
+    y[2] = __uint_as_float((uint32_t)b[1] << 16);
+    y[3] = __uint_as_float((uint32_t)b[1] & 0xFFFF0000u);
+    *(v4f*)(yslot + row * d + c) = y;
+  }
+}
+
 // Per token: dw[t, j] = <dy[t], Yslot[t, j]> (reverse-combine of the weights), then the
 // gradient of the selected logits.  One 256-thread workgroup per token: thread i holds dy at
 // columns 4(i + 256m) in registers and reads each slot row with 16-byte loads, so a token's
@@ -177,6 +197,12 @@ unsigned grid_for(int64_t n) {
 }
 
 }  // namespace
+
+hipError_t launch_identity_slots(const uint16_t* x, int T, int slots, int d, float* yslot, hipStream_t st) {
+  hipLaunchKernelGGL(k_identity_slots, dim3(grid_for((int64_t)T * slots * d / 4)), dim3(256), 0, st, x, T, slots, d,
+                     yslot);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const float* yslot, const float* w, int T, int k, int S, int d, uint16_t* y_bf16,
                           float* y_f32, hipStream_t st) {

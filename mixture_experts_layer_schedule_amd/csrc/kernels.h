@@ -128,6 +128,8 @@ struct SchedBuild {
 hipError_t launch_schedule(const SchedBuild&, hipStream_t);
 
 // Combine and backward helpers.
+// Combine check mode: yslot[t, j, :] = x[t, :] (bf16 widened exactly) for all j < slots.
+hipError_t launch_identity_slots(const uint16_t* x, int T, int slots, int d, float* yslot, hipStream_t);
 hipError_t launch_combine(const float* yslot, const float* w, int T, int k, int S, int d, uint16_t* y_bf16,
                           float* y_f32, hipStream_t);
 hipError_t launch_router_bwd(const uint16_t* dy, const float* yslot, const float* logits, const int32_t* idx,

@@ -155,3 +155,20 @@ def test_sampled_token_end_to_end(run, t):
     assert np.array_equal(to_np(layer.saved_tensor("idx")[t]), fw.idx[0])
     _check(f"y[{t}]", to_np(layer.y32[t:t + 1]), fw.y, fenv.By)
     _check(f"dx[{t}]", to_np(layer.dx32[t:t + 1]), bw.dx, benv.Bdx)
+
+
+def test_bitwise_run_to_run(run):
+    """A second forward + backward of the same inputs reproduces every output bit for bit (fixed
+    summation orders, no atomics), in the default two-stream backward schedule."""
+    import torch
+    cfg, inp, layer, experts = run
+    outs = lambda: (layer.y, layer.y32, layer.dx, layer.dx32, layer.dw_r, layer.dw1, layer.dw2)  # noqa: E731
+    ref = [t.clone() for t in outs()]
+    log("dsv3: second forward + backward")
+    layer.forward()
+    layer.backward()
+    torch.cuda.synchronize()
+    for name, r, t in zip(("y", "y32", "dx", "dx32", "dw_r", "dw1", "dw2"), ref, outs()):
+        assert torch.equal(r, t), name
+    del ref
+    torch.cuda.empty_cache()

@@ -158,16 +158,38 @@ def test_backward_outputs(pair, env):
 def test_bitwise_reproducible(pair):
     cfg, inp, fw, bw, layer = pair
     import torch
-    y0 = layer.y32.clone()
-    dx0 = layer.dx32.clone()
-    dw10 = layer.dw1.clone()
-    for _ in range(3):
+    ref = [t.clone() for t in (layer.y32, layer.y, layer.dx32, layer.dw_r, layer.dw1, layer.dw2)]
+    for _ in range(10):
         layer.forward()
         layer.backward()
+        torch.cuda.synchronize()
+        for r, t in zip(ref, (layer.y32, layer.y, layer.dx32, layer.dw_r, layer.dw1, layer.dw2)):
+            assert torch.equal(r, t)
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
+def test_identity_experts_return_x(cfg):
+    """Identity experts with unit-sum combine weights (plus weight-1 shared experts): the layer
+    returns (1 + n_shared) x, bit for bit in bf16 (a sum of k weights is 1 within a few float32
+    ulps, far inside half a bf16 ulp), on the GPU's own routing."""
+    import torch
+    import mixture_experts_layer_schedule_amd as moe
+    from mixture_experts_layer_schedule_amd import MoeLayer
+    inp = moe_inputs.layer_inputs(cfg, with_dy=True)
+    layer = MoeLayer.from_config(cfg, with_backward=True, flags=moe.MOE_F_IDENTITY_EXPERTS)
+    layer.set_inputs(inp.x_bits, inp.w_r_bits, inp.bias, inp.dy_bits)
+    layer.load_experts(moe_inputs.iter_expert_weights(cfg))
+    layer.forward()
     torch.cuda.synchronize()
-    assert torch.equal(y0, layer.y32)
-    assert torch.equal(dx0, layer.dx32)
-    assert torch.equal(dw10, layer.dw1)
+    x = torch.from_numpy(inp.x_bits.view(np.int16)).view(torch.bfloat16).float()
+    ref = (1 + cfg.n_shared) * x  # exact
+    assert torch.equal(layer.y.cpu().view(torch.int16), ref.to(torch.bfloat16).view(torch.int16))
+    y32 = layer.y32.cpu()
+    assert torch.all((y32 - ref).abs() <= 2.0 ** -20 * ref.abs())
+    w = to_np(layer.saved_tensor("w"))
+    assert np.max(np.abs(w.sum(axis=1) - 1.0)) <= 4 * 2.0 ** -24 * cfg.k
+    with pytest.raises(moe.MoeError):
+        layer.backward()
 
 
 def test_serial_and_concurrent_backward_identical(pair):

@@ -50,7 +50,7 @@ def test_query_layout_is_aligned_and_ordered():
     (dict(chunk_rows=128), moe.MOE_ESHAPE),
     (dict(producer_wgs=129), moe.MOE_ESHAPE),
     (dict(flags=3), moe.MOE_EINVAL),         # direct gather and ring dispatch together
-    (dict(flags=8), moe.MOE_EINVAL),         # unknown flag
+    (dict(flags=16), moe.MOE_EINVAL),        # unknown flag
 ])
 def test_query_rejects_bad_config(kw, status):
     base = dict(T=256, d=256, E=8, k=2, inter=128)
@@ -62,7 +62,7 @@ def test_query_rejects_bad_config(kw, status):
     assert ei.value.status == status
 
 
-@pytest.mark.parametrize("flags", [0, 1, 4, 5])
+@pytest.mark.parametrize("flags", [0, 1, 4, 5, 8, 9])
 def test_query_accepts_schedule_flags(flags):
     """Direct gather (1) and the launch-order backward (4) are valid alone and together."""
     ws, _ = moe.moe_query(moe.make_config(256, 256, 8, 2, 128, flags=flags))
