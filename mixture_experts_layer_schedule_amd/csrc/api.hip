@@ -29,7 +29,7 @@ Dims dims(const moe_config& c) {
   m.NX = m.E + m.S;
   m.R = m.T * m.k;
   m.RS = m.R + m.S * m.T;
-  m.nblk = (m.T + 255) / 256;
+  m.nblk = (m.T + kSchedBlockTokens - 1) / kSchedBlockTokens;
   m.ld_tok = (int64_t)up((size_t)(m.RS + 127 * m.NX), 128);
   m.tiles_bound = m.RS / 256 + m.NX + 1;  // sum over experts of ceil(count / 256)
   m.tile64_bound = m.ld_tok / 64;

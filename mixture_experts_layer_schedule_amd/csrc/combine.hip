@@ -134,28 +134,39 @@ __global__ __launch_bounds__(256) void k_router_bwd(const uint16_t* __restrict__
   }
 }
 
-// dW_r[e, n] = sum over the expert's routed rows (increasing token order) of dL * x[t, n].  The
-// rows' indices and values are loaded 8 at a time ahead of the (in-order) accumulation.
-__global__ __launch_bounds__(256) void k_router_wgrad(SchedView s, const float* __restrict__ dl,
+// dW_r[e, n] = sum over the expert's routed rows (increasing token order) of dL * x[t, n].  A
+// thread owns 8 consecutive columns, so each routed row is one 16-byte load of x; the rows'
+// indices and values are loaded 8 at a time ahead of the (in-order) accumulation.
+__global__ __launch_bounds__(128) void k_router_wgrad(SchedView s, const float* __restrict__ dl,
                                                       const uint16_t* __restrict__ x, int d, float* __restrict__ dwr) {
   const int e = blockIdx.y;
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= d) return;
-  float acc = 0.0f;
+  const int c8 = blockIdx.x * blockDim.x + threadIdx.x;  // columns [8 c8, 8 c8 + 8)
+  if (c8 * 8 >= d) return;
+  float acc[8];
+  static_for<8>([&]<int c>() { acc[c] = 0.0f; });
   const int r0 = s.offsets[e], r1 = s.offsets[e + 1];
   for (int r = r0; r < r1; r += 8) {
     int sid[8];
-    float dv[8], xv[8];
+    float dv[8];
+    v4i xv[8];
     static_for<8>([&]<int u>() { sid[u] = r + u < r1 ? s.perm[r + u] : s.perm[r]; });
     static_for<8>([&]<int u>() {
       dv[u] = dl[sid[u]];
-      xv[u] = bf16_to_f32(x[(size_t)(sid[u] / s.k) * d + n]);
+      xv[u] = *(const v4i*)(x + (size_t)(sid[u] / s.k) * d + 8 * c8);
     });
     static_for<8>([&]<int u>() {
-      if (r + u < r1) acc += dv[u] * xv[u];
+      if (r + u < r1) {
+        static_for<8>([&]<int c>() {
+          const uint32_t wd = (uint32_t)xv[u][c >> 1];
+          const float xf = __uint_as_float((c & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
+          acc[c] += dv[u] * xf;
+        });
+      }
     });
   }
-  dwr[(size_t)e * d + n] = acc;
+  float* o = dwr + (size_t)e * d + 8 * c8;
+  *(v4f*)o = (v4f){acc[0], acc[1], acc[2], acc[3]};
+  *(v4f*)(o + 4) = (v4f){acc[4], acc[5], acc[6], acc[7]};
 }
 
 // dx[t, n] = sum_j dXslot[t, j, n] + sum_s dXslot[t, k + s, n] + sum_j dL[t, j] W_r[idx[t, j], n].
@@ -221,7 +232,7 @@ hipError_t launch_router_bwd(const uint16_t* dy, const float* yslot, const float
 
 hipError_t launch_router_wgrad(const SchedView& s, const float* dl, const uint16_t* x, int d, int E, float* dw_r,
                                hipStream_t st) {
-  hipLaunchKernelGGL(k_router_wgrad, dim3((d + 255) / 256, E), dim3(256), 0, st, s, dl, x, d, dw_r);
+  hipLaunchKernelGGL(k_router_wgrad, dim3((d / 8 + 127) / 128, E), dim3(128), 0, st, s, dl, x, d, dw_r);
   return hipGetLastError();
 }
 

@@ -6,6 +6,9 @@
 namespace moe {
 
 // Device-side view of the schedule built by the router/schedule kernels.
+// Tokens per block of the schedule builder (per-block expert histograms, scanned per expert).
+constexpr int kSchedBlockTokens = 64;
+
 struct SchedView {
   const int32_t* perm;        // [R] slot id t*k + j of each routed permuted row
   const int32_t* offsets;     // [n_exp + 1] first permuted row of each expert

@@ -32,20 +32,32 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
   v16f acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-  for (int k0 = 0; k0 < d; k0 += 64) {
-    v8bf a[4], b[4];
+  // The operands of step k0 + 64 are loaded before the matrix instructions of step k0, so each
+  // step's load latency overlaps the previous step's products (the summation order is unchanged).
+  v8bf a[4], b[4], na[4], nb[4];
+  auto load = [&](int k0, v8bf (&ra)[4], v8bf (&rb)[4]) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      a[s] = *(const v8bf*)(pa + k0 + 8 * s);
-      v8bf bb = *(const v8bf*)(pb + k0 + 8 * s);
-      if (!evalid) {
+      ra[s] = *(const v8bf*)(pa + k0 + 8 * s);
+      rb[s] = *(const v8bf*)(pb + k0 + 8 * s);
+    }
+  };
+  load(0, a, b);
+  for (int k0 = 0; k0 < d; k0 += 64) {
+    if (k0 + 64 < d) load(k0 + 64, na, nb);
+    if (!evalid) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) bb[j] = (__bf16)0.0f;
-      }
-      b[s] = bb;
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) b[s][j] = (__bf16)0.0f;
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b[s], acc, 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      a[s] = na[s];
+      b[s] = nb[s];
+    }
   }
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
@@ -119,20 +131,20 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ L, int T
 
 // ----------------------------------------------------------------------------- schedule
 //
-// Expert-major stable permutation of the T*k routed slots in three passes: per 256-token block
+// Expert-major stable permutation of the T*k routed slots in three passes: per 64-token block
 // counts, a per-expert exclusive scan over blocks plus the expert offsets, and a scatter in which
 // one thread per expert walks its block's tokens in order.  Shared experts own the rows after
 // the routed ones (all T tokens, in order).
 
-constexpr int kBlkTok = 256;
+constexpr int kBlkTok = kSchedBlockTokens;
 
 __global__ __launch_bounds__(256) void k_sched_hist(SchedBuild p) {
   extern __shared__ int32_t cnt[];
   for (int e = threadIdx.x; e < p.E; e += blockDim.x) cnt[e] = 0;
   __syncthreads();
-  const int t = blockIdx.x * kBlkTok + threadIdx.x;
-  if (t < p.T)
-    for (int j = 0; j < p.k; ++j) atomicAdd(&cnt[p.idx[(size_t)t * p.k + j]], 1);
+  const int t0 = blockIdx.x * kBlkTok;
+  const int n = min(kBlkTok, p.T - t0) * p.k;  // the block's (token, slot) entries
+  for (int q = threadIdx.x; q < n; q += blockDim.x) atomicAdd(&cnt[p.idx[(size_t)t0 * p.k + q]], 1);
   __syncthreads();
   for (int e = threadIdx.x; e < p.E; e += blockDim.x) p.blkcnt[(size_t)blockIdx.x * p.E + e] = cnt[e];
 }
