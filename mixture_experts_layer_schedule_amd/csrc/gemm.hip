@@ -1,6 +1,7 @@
 // Grouped MXFP8 GEMMs of the expert FFN (forward, dgrad and wgrad) on gfx950; the tile core is
 // in gemm_core.h.  The routed GEMMs run one (row tile, 256-column tile) item per workgroup; the
-// row count of the item picks the instantiation with that many 32-row fragments.
+// row count of the item picks the instantiation with that many 32-row fragments.  The forward
+// GEMMs run the tile with 8 waves (two per SIMD, 512 threads), the backward ones with 4.
 #include "common.h"
 #include "gemm_core.h"
 #include "kernels.h"
@@ -42,7 +43,7 @@ MOE_DEV const int64_t* row_slot_table(const SchedView& s, const RowTile& rt, uin
 // schedule), epilogue h = silu(G) U quantised along I.  A column tile is 128 I columns: for
 // each wave 32 gate rows of W1 and the matching 32 up rows.
 
-__global__ __launch_bounds__(256, 1) void k_gemm_gateup(GateUpArgs p) {
+__global__ __launch_bounds__(512, 1) void k_gemm_gateup(GateUpArgs p) {
   extern __shared__ __align__(16) uint8_t lds[];
   const SchedView& s = p.s;
   const int I = p.I, d = p.d, NT = I / 128;
@@ -56,21 +57,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_gateup(GateUpArgs p) {
   const uint8_t* w1s = p.w1s + (size_t)rt.e * 2 * I * (d / 32);
   const int last = rt.rows - 1;
   dispatch_rows(rt.rows, [&]<int F>() {
-    TileLoads<F> L;
+    TileLoads8<F> L;
     L.init(p.xq, [&](int r) { return p.xq + (size_t)row_token(s, rt.r0 + min(r, last)) * d; },
            w1, [&](int r) { return w1 + (size_t)gateup_brow(r, n0, I) * d; },
            p.xs, [&](int r) { return p.xs + (size_t)row_token(s, rt.r0 + min(r, last)) * (d / 32); },
            w1s, [&](int r) { return w1s + (size_t)gateup_brow(r, n0, I) * (d / 32); });
-    v16f acc[F][2];
-    mainloop<F, kStages>(lds, L, d / KS, acc);
-    gateup_epilogue<F>(acc, rt.r0, rt.rows, n0, I, p.g, p.u, p.hq, p.hs);
+    v16f acc[(F + 1) / 2][2];
+    mainloop8<F>(lds, L, d / KS, acc);
+    gateup_epilogue8<F>(acc, rt.r0, rt.rows, n0, I, p.g, p.u, p.hq, p.hs);
   });
 }
 
 // ---------------------------------------------------------------------------------------------
 // Forward down: Y_r = H_r W2_e^T, pushed to its slot Yslot[t, j] (push combine).
 
-__global__ __launch_bounds__(256, 1) void k_gemm_down(DownArgs p) {
+__global__ __launch_bounds__(512, 1) void k_gemm_down(DownArgs p) {
   extern __shared__ __align__(16) uint8_t lds[];
   const SchedView& s = p.s;
   const int I = p.I, d = p.d, NT = (d + TN - 1) / TN;
@@ -83,27 +84,29 @@ __global__ __launch_bounds__(256, 1) void k_gemm_down(DownArgs p) {
   const uint8_t* w2 = p.w2q + (size_t)rt.e * d * I;
   const uint8_t* w2s = p.w2s + (size_t)rt.e * d * (I / 32);
   const int last = rt.rows - 1;
-  const int w = threadIdx.x >> 6, l = lane_id(), i = l & 31, h = l >> 5;
-  const bool active = n0 + 64 * w < d;
+  const int w = threadIdx.x >> 6, l = lane_id(), i = l & 31, h = l >> 5, wc = w & 3;
+  const bool active = n0 + 64 * wc < d;
   dispatch_rows(rt.rows, [&]<int F>() {
-    TileLoads<F> L;
+    constexpr int FH = (F + 1) / 2;
+    const int m0 = (w >> 2) * FH;
+    TileLoads8<F> L;
     const uint8_t* ha = p.hq + (size_t)rt.r0 * I;
     const uint8_t* hsa = p.hs + (size_t)rt.r0 * (I / 32);
     L.init(ha, [&](int r) { return ha + (size_t)min(r, last) * I; },
            w2, [&](int r) { return w2 + (size_t)min(n0 + r, d - 1) * I; },
            hsa, [&](int r) { return hsa + (size_t)min(r, last) * (I / 32); },
            w2s, [&](int r) { return w2s + (size_t)min(n0 + r, d - 1) * (I / 32); });
-    v16f acc[F][2];
-    mainloop<F, kStages>(lds, L, I / KS, acc);
+    v16f acc[FH][2];
+    mainloop8<F>(lds, L, I / KS, acc);
     const int64_t* slot = row_slot_table(s, rt, lds + ((I / KS) % kStages) * STAGE_BYTES);
     if (!active) return;
-    static_for<F>([&]<int mi>() {
+    static_for<FH>([&]<int m>() {
       static_for<16>([&]<int v>() {
-        const int r = 32 * mi + 8 * (v >> 2) + 4 * h + (v & 3);
+        const int r = 32 * (m0 + m) + 8 * (v >> 2) + 4 * h + (v & 3);
         if (r < rt.rows) {
-          float* dst = p.yslot + slot[r] * d + n0 + 64 * w + i;
-          dst[0] = acc[mi][0][v];
-          dst[32] = acc[mi][1][v];
+          float* dst = p.yslot + slot[r] * d + n0 + 64 * wc + i;
+          dst[0] = acc[m][0][v];
+          dst[32] = acc[m][1][v];
         }
       });
     });
@@ -279,12 +282,12 @@ size_t gemm_lds_bytes() { return lds_bytes_for(kStages); }
 static size_t wgrad_lds_bytes() { return lds_bytes_for(2); }
 
 hipError_t launch_gemm_gateup(const GateUpArgs& a, int tiles_bound, hipStream_t st) {
-  hipLaunchKernelGGL(k_gemm_gateup, dim3(tiles_bound * (a.I / 128)), dim3(256), gemm_lds_bytes(), st, a);
+  hipLaunchKernelGGL(k_gemm_gateup, dim3(tiles_bound * (a.I / 128)), dim3(512), gemm_lds_bytes(), st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_down(const DownArgs& a, int tiles_bound, hipStream_t st) {
-  hipLaunchKernelGGL(k_gemm_down, dim3(tiles_bound * ((a.d + TN - 1) / TN)), dim3(256), gemm_lds_bytes(), st, a);
+  hipLaunchKernelGGL(k_gemm_down, dim3(tiles_bound * ((a.d + TN - 1) / TN)), dim3(512), gemm_lds_bytes(), st, a);
   return hipGetLastError();
 }
 

@@ -436,6 +436,128 @@ MOE_DEV void mainloop_tb(uint8_t* lds, const TileLoads<F>& L, TransB& tb, int nk
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Two waves per SIMD (the forward and weight-gradient GEMMs).  A workgroup with one wave per
+// SIMD keeps one stage (64 KB) of loads in flight and a wave's loads return at a bounded rate,
+// so the loop above spends most of each stage waiting for its loads (measured: about 1.5 us per
+// 64 KB per workgroup even from L2, while two workgroups per compute unit move twice as much).
+// Here 512 threads (8 waves, two per SIMD) share the same 256 x 256 tile and its loads: wave w
+// owns the column group wc = w % 4 (columns [64 wc, 64 wc + 64) as two fragments, as in the
+// 4-wave tile) and the row half wr = w / 4 (row fragments [wr FH, wr FH + FH), FH = ceil(F / 2)),
+// so each wave holds FH x 2 accumulator tiles (at most 128 registers).  With an odd F the last
+// fragment of the upper half lies past the tile: it multiplies stale LDS rows and its results
+// are dropped.  Loads: the 4F A and 32 B instructions of a stage are dealt to the 8 waves in
+// turn; waves 0-3 load the A scale words, waves 4-7 the B ones.  The stage layout is the 4-wave
+// core's.
+
+template <int F>
+struct TileLoads8 {
+  static constexpr int NA = (4 * F + 7) / 8;  // A instructions per wave (q = w + 8u < 4F)
+  const uint8_t *abase, *bbase, *asbase, *bsbase;
+  uint32_t a[NA];
+  uint32_t b[4];
+  uint32_t sc;  // A scale word of row 64w + l (w < 4) or B scale word of row 64(w - 4) + l
+
+  template <class ARow, class BRow, class ASRow, class BSRow>
+  MOE_DEV void init(const uint8_t* ab, ARow a_rows, const uint8_t* bb, BRow b_rows, const uint8_t* asb,
+                    ASRow a_srows, const uint8_t* bsb, BSRow b_srows) {
+    abase = ab; bbase = bb; asbase = asb; bsbase = bsb;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int sub = l >> 3, slot = l & 7;
+    static_for<NA>([&]<int u>() {
+      const int r = 8 * min(w + 8 * u, 4 * F - 1) + sub;
+      a[u] = (uint32_t)(a_rows(r) - ab) + 16 * (slot ^ swz(r));
+    });
+    static_for<4>([&]<int u>() {
+      const int r = 8 * (w + 8 * u) + sub;
+      b[u] = (uint32_t)(b_rows(r) - bb) + 16 * (slot ^ swz(r));
+    });
+    sc = w < 4 ? (uint32_t)(a_srows(64 * w + l) - asb) : (uint32_t)(b_srows(64 * (w - 4) + l) - bsb);
+  }
+};
+
+// Loads of stage t into buffer t % 2: one scale word and this wave's share of the data.
+template <int F>
+MOE_DEV void issue_stage8(const TileLoads8<F>& L, uint8_t* lds, int t) {
+  const int w = threadIdx.x >> 6;
+  const uint32_t k0 = (uint32_t)t * KS;
+  uint8_t* st = lds + (t % 2) * STAGE_BYTES;
+  uint8_t* scp = st + DATA_BYTES;
+  if (w < 4)
+    lds_load4<0>(L.asbase + (L.sc + (k0 >> 5)), scp + 256 * w);
+  else
+    lds_load4<0>(L.bsbase + (L.sc + (k0 >> 5)), scp + TM * 4 + 256 * (w - 4));
+  static_for<TileLoads8<F>::NA>([&]<int u>() {
+    const int q = w + 8 * u;
+    if (q < 4 * F) lds_load16<0>(L.abase + (L.a[u] + k0), st + 1024 * q);
+  });
+  static_for<4>([&]<int u>() { lds_load16<0>(L.bbase + (L.b[u] + k0), st + A_STAGE + 1024 * (w + 8 * u)); });
+}
+
+// Multiply one staged K slice (two MFMA steps) for this wave's FH row fragments and two column
+// fragments; A fragments read two at a time ahead of the matrix instructions.
+template <int F>
+MOE_DEV void compute_stage8(const uint8_t* st, v16f (&acc)[(F + 1) / 2][2]) {
+  constexpr int FH = (F + 1) / 2;
+  const int l = lane_id(), i = l & 31, h = l >> 5, w = threadIdx.x >> 6;
+  const int wc = w & 3, m0 = (w >> 2) * FH;
+  const int sw = swz(i);
+  const uint32_t* sc = (const uint32_t*)(st + DATA_BYTES);
+  int sa[FH], sb[2];
+  static_for<FH>([&]<int m>() { sa[m] = (int)(sc[32 * (m0 + m) + i] >> (8 * h)); });
+  sb[0] = (int)(sc[TM + 64 * wc + i] >> (8 * h));
+  sb[1] = (int)(sc[TM + 64 * wc + 32 + i] >> (8 * h));
+  constexpr int NG = (FH + 1) / 2;
+  static_for<2>([&]<int kk>() {
+    auto frag = [&](const uint8_t* rp, int s2) {
+      const v4i lo = *(const v4i*)(rp + 16 * ((4 * kk + h) ^ s2));
+      const v4i hi = *(const v4i*)(rp + 16 * ((4 * kk + 2 + h) ^ s2));
+      return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    auto afrag = [&](int m) { return frag(st + (32 * (m0 + m) + i) * KS, sw ^ (4 * ((m0 + m) & 1))); };
+    const v8i b0 = frag(st + A_STAGE + (64 * wc + i) * KS, sw);
+    const v8i b1 = frag(st + A_STAGE + (64 * wc + 32 + i) * KS, sw ^ 4);
+    v8i pair[NG + 1][2];
+    static_for<2>([&]<int j>() {
+      if constexpr (j < FH) pair[0][j] = afrag(j);
+    });
+    static_for<NG>([&]<int g>() {
+      static_for<2>([&]<int j>() {
+        constexpr int m = 2 * (g + 1) + j;
+        if constexpr (m < FH) pair[g + 1][j] = afrag(m);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<2>([&]<int j>() {
+        constexpr int m = 2 * g + j;
+        if constexpr (m < FH) {
+          const int s_a = sa[m] >> (16 * kk);
+          acc[m][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pair[g][j], b0, acc[m][0], 0, 0, 0, s_a, 0,
+                                                                       sb[0] >> (16 * kk));
+          acc[m][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pair[g][j], b1, acc[m][1], 0, 0, 0, s_a, 0,
+                                                                       sb[1] >> (16 * kk));
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  });
+}
+
+// acc = this wave's part of A_tile * B_tile^T over K = 128 nk; one barrier per stage.
+template <int F>
+MOE_DEV void mainloop8(uint8_t* lds, const TileLoads8<F>& L, int nk, v16f (&acc)[(F + 1) / 2][2]) {
+  static_for<(F + 1) / 2>([&]<int m>() {
+    acc[m][0] = (v16f){};
+    acc[m][1] = (v16f){};
+  });
+  if (nk <= 0) return;
+  issue_stage8<F>(L, lds, 0);
+  for (int t = 0; t < nk; ++t) {
+    wait_loads_and_sync<0>();  // stage t has landed; every wave is done with stage t - 1
+    if (t + 1 < nk) issue_stage8<F>(L, lds, t + 1);
+    compute_stage8<F>(lds + (t % 2) * STAGE_BYTES, acc);
+  }
+}
+
 // Quantise 32 consecutive columns of one row held by the 32 lanes of a half-wave:
 // returns this lane's code; *scale receives the block's e8m0 byte.
 MOE_DEV uint32_t quant_lane32(float v, uint32_t* scale) {
@@ -463,6 +585,33 @@ MOE_DEV void gateup_epilogue(const v16f (&acc)[F][2], int r0, int rows, int n0, 
     static_for<16>([&]<int v>() {
       const int r = 32 * mi + 8 * (v >> 2) + 4 * h + (v & 3);
       const float g = acc[mi][0][v], u = acc[mi][1][v];
+      uint32_t sc;
+      const uint32_t code = quant_lane32(silu(g) * u, &sc);
+      if (r < rows) {
+        const size_t o = (size_t)(r0 + r) * I + n;
+        g_out[o] = g;
+        u_out[o] = u;
+        hq[o] = (uint8_t)code;
+        if (i == 0) hs[(size_t)(r0 + r) * (I / 32) + (n >> 5)] = (uint8_t)sc;
+      }
+      if ((v & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the registers in flight
+    });
+  });
+}
+
+// The gate/up epilogue for the 8-wave tile: this wave's FH row fragments (from m0) of the
+// column group wc.
+template <int F>
+MOE_DEV void gateup_epilogue8(const v16f (&acc)[(F + 1) / 2][2], int r0, int rows, int n0, int I, float* g_out,
+                              float* u_out, uint8_t* hq, uint8_t* hs) {
+  constexpr int FH = (F + 1) / 2;
+  const int l = lane_id(), i = l & 31, h = l >> 5, w = threadIdx.x >> 6;
+  const int wc = w & 3, m0 = (w >> 2) * FH;
+  const int n = n0 + 32 * wc + i;
+  static_for<FH>([&]<int m>() {
+    static_for<16>([&]<int v>() {
+      const int r = 32 * (m0 + m) + 8 * (v >> 2) + 4 * h + (v & 3);
+      const float g = acc[m][0][v], u = acc[m][1][v];
       uint32_t sc;
       const uint32_t code = quant_lane32(silu(g) * u, &sc);
       if (r < rows) {
