@@ -32,7 +32,8 @@ def log(*a):
 
 # ----------------------------------------------------------------------------- algorithmic work
 #
-# Bytes and flops each phase must move / compute (the design doc derives them).  R = T*k routed rows,
+# Bytes and flops each phase must move / compute: weights once per GEMM pass, activations once in
+# and once out per stage, dW once, the dense E-times work not counted.  R = T*k routed rows,
 # NX experts; weights are MXFP8 (1 byte + 1/32 scale byte per value); activations as stored.
 
 def phase_work(cfg, tok_pad: int) -> dict:
@@ -205,7 +206,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one MI355X: the layer runs with every expert resident on a single GPU; "
-              "runs on more than one GPU are not part of this build (use --gpus 1).", file=sys.stderr)
+              "it has no multi-GPU mode (use --gpus 1).", file=sys.stderr)
         return 2
 
     import numpy as np

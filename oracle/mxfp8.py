@@ -14,7 +14,7 @@ Microscaling v1.0 definition:
 * each element is a / X converted to e4m3 with round-to-nearest-even and
   saturation to +-448.
 
-Readings where the format leaves a choice (listed in the design doc as well):
+Readings where the format leaves a choice:
 * an all-zero block takes scale byte 0 (2**-127) and zero codes;
 * the exponent is clamped to the e8m0 range [-127, 127];
 * the sign of a code is the sign bit of the input, so an input that rounds to
