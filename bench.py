@@ -197,6 +197,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="dsv3_fwd_bwd")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="override the workload's token count T (a T sweep; the default workload is unchanged)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-experts", type=int, default=2)
     ap.add_argument("--dominant", default="auto", help="phase reported in roofline (default: longest)")
@@ -219,6 +221,8 @@ def main() -> int:
     cfg = moe_inputs.CONFIGS[args.config]
     if not cfg.backward:
         cfg = cfg.with_(backward=True)
+    if args.tokens:
+        cfg = cfg.with_(T=args.tokens, name=f"{cfg.name}_T{args.tokens}")
     t0 = time.time()
     inp = moe_inputs.layer_inputs(cfg, with_dy=True)
     layer = MoeLayer.from_config(cfg, with_backward=True, flags=args.flags)
