@@ -13,7 +13,8 @@
  * Conventions for every entry point
  *   - Pointers are device pointers unless stated otherwise; the caller allocates and frees
  *     every buffer.  The library never allocates device memory, never frees, and never
- *     synchronises the host: work is enqueued on the caller's stream and the call returns.
+ *     synchronises the host inside moe_fwd / moe_bwd: work is enqueued on the caller's stream
+ *     and the call returns (knowledge card, 方法/产品要点: no CPU-GPU synchronisation).
  *   - Tensors are dense, row-major, contiguous.  "bf16" is bfloat16 stored as uint16_t,
  *     "fp8" is OCP e4m3 ("fn") stored as uint8_t, "e8m0" is a biased-127 exponent byte.
  *   - MXFP8: a tensor quantised along an axis holds fp8 codes of the same shape plus one
@@ -21,6 +22,9 @@
  *   - Argument errors are detected on the host before anything is enqueued and returned as a
  *     moe_status; nothing is launched then.  Launch failures return MOE_ELAUNCH.
  *   - Tensor pointers must be 16-byte aligned; `saved` and `workspace` 256-byte aligned.
+ *   - Concurrency: calls on different streams may overlap as long as they use different
+ *     `saved` and `workspace` buffers.  moe_set_phase_events is process-wide and meant for
+ *     single-threaded measurement.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -38,10 +42,16 @@ typedef enum moe_status {
   MOE_EINVAL = 1,      /* null pointer or unsupported option */
   MOE_ESHAPE = 2,      /* sizes outside the supported set (see moe_config) */
   MOE_EALIGN = 3,      /* a pointer is not aligned as required */
-  MOE_EWORKSPACE = 4,  /* reserved: workspace smaller than moe_query reports */
+  MOE_EWORKSPACE = 4,  /* `saved` or `workspace` smaller than moe_query reports */
   MOE_ELAUNCH = 5,     /* a kernel launch failed */
   MOE_EDEVICE = 6      /* reported by moe_device_status: the device flagged an anomaly */
 } moe_status;
+
+/* Codes the device writes into the workspace status word (read with moe_device_status).  The
+ * word is sticky: a later call does not clear it. */
+#define MOE_DEV_RING_TIMEOUT 1   /* a bounded wait of the ring dispatch kernel expired */
+#define MOE_DEV_NONFINITE_LOGIT 2 /* a router logit was NaN or infinite (its token is still
+                                     routed to k distinct valid experts; NaN ranks as -inf) */
 
 typedef enum moe_score_fn {
   MOE_SCORE_SOFTMAX = 0, /* softmax over the k selected logits */
@@ -49,10 +59,13 @@ typedef enum moe_score_fn {
 } moe_score_fn;
 
 /* Layer shape and tuning.  Supported: T >= 1; d and inter multiples of 128; 1 <= k <= 16;
- * k <= E <= 512; n_shared in {0, 1}.  The tuning fields (ring_rows, chunk_rows, producer_wgs)
- * correspond to the pages' per-workload knobs (buffer capacity, minibatch and number of
- * communication SMs: article section "2.37 倍同 1.41 倍係兩份成績"); 0 picks a default.  They
- * never change results. */
+ * k <= E <= 512; n_shared in {0, 1}; T*(k + n_shared) < 2^30; T*d < 2^32; 2*inter*d < 2^32;
+ * the token-axis operand stride of the weight-gradient GEMMs (about T*(k + n_shared) + 128*(E +
+ * n_shared)) below 2^24 (several kernels address an operand with 32-bit byte offsets).
+ * The tuning fields are the pages' per-workload knobs (buffer capacity, minibatch and number of
+ * communication SMs: article "Cursor 為 Composer 改造 MoE 訓練…", section "2.37 倍同 1.41 倍係兩份
+ * 成績"); they only act on the ring dispatch (MOE_F_RING_DISPATCH) and must be 0 otherwise.  0
+ * picks a default.  They never change results. */
 typedef struct moe_config {
   int32_t T;          /* tokens */
   int32_t d;          /* hidden size */
@@ -77,11 +90,11 @@ typedef struct moe_config {
 
 /* Backward schedule.  By default moe_bwd runs the branch that needs only the forward's saved
  * rows and dy (token-axis requantisation of X, H and w*dY, then dW2) on a second stream of the
- * device, created by the library on first use with default priority and kept until the process
- * ends, beside the router backward and the dgrad chain; the caller's stream waits for it before
- * dW1, so the call stays ordered on the caller's stream as a whole.  MOE_F_SERIAL_BWD runs every
- * kernel in launch order on the caller's stream instead (phase timing then covers every phase;
- * results are identical either way). */
+ * device, created by the library on first use in each host thread with default priority and
+ * kept until the process ends, beside the router backward and the dgrad chain; the caller's
+ * stream waits for it before dW1, so the call stays ordered on the caller's stream as a whole.
+ * MOE_F_SERIAL_BWD runs every kernel in launch order on the caller's stream instead (phase
+ * timing then covers every phase; results are identical either way). */
 #define MOE_F_SERIAL_BWD 4u
 
 /* Check mode of the combine: every expert is replaced by the identity (the row of expert e for
@@ -93,9 +106,15 @@ typedef struct moe_config {
  * moe_bwd rejects the flag with MOE_EINVAL (there is no saved expert state to differentiate). */
 #define MOE_F_IDENTITY_EXPERTS 8u
 
+/* Forward only: moe_fwd skips what only the backward pass reads (the transposed requantised
+ * expert weights w1t / w2t of the saved buffer, which then take no space); moe_bwd rejects the
+ * flag with MOE_EINVAL. */
+#define MOE_F_FORWARD_ONLY 16u
+
 /* Byte offsets inside the caller-owned `saved` buffer that moe_fwd fills and moe_bwd reads
- * (the schedule is built once and reused by the backward pass).  R = T*k routed rows,
- * RS = R + n_shared*T rows in expert-major ("permuted") order, S = n_shared, NX = E + S. */
+ * (the schedule is built once and reused by the backward pass: knowledge card, 方法/产品要点).
+ * R = T*k routed rows, RS = R + n_shared*T rows in expert-major ("permuted") order,
+ * S = n_shared, NX = E + S. */
 typedef struct moe_saved_layout {
   size_t logits;     /* float [T, E]       router logits (+ bias) */
   size_t idx;        /* int32 [T, k]       selected experts, best first */
@@ -115,68 +134,114 @@ typedef struct moe_saved_layout {
   size_t hq;         /* fp8   [RS, I]      silu(g) * u quantised along I */
   size_t hs;         /* e8m0  [RS, I/32] */
   size_t yslot;      /* float [T, k + S, d] expert output of every (token, slot) */
+  size_t w1t;        /* fp8   [NX, d, 2I]  W1 transposed, requantised along 2I (experts with rows) */
+  size_t w1ts;       /* e8m0  [NX, d, 2I/32] */
+  size_t w2t;        /* fp8   [NX, I, d]   W2 transposed, requantised along d (experts with rows) */
+  size_t w2ts;       /* e8m0  [NX, I, d/32] */
   size_t total;      /* bytes of `saved` */
 } moe_saved_layout;
 
-/* Sizes of the caller-owned buffers for `cfg`: *workspace_bytes for the workspace shared by
- * moe_fwd and moe_bwd, *saved for the layout of the saved buffer.  Host-only; no GPU needed. */
-moe_status moe_query(const moe_config* cfg, size_t* workspace_bytes, moe_saved_layout* saved);
+/* Byte offsets inside the caller-owned `workspace` (scratch of moe_fwd and moe_bwd; exported
+ * so that tests can read the stage results of the backward pass).  ld = tok_stride. */
+typedef struct moe_workspace_layout {
+  size_t status;     /* int32              device status word (MOE_DEV_*), sticky */
+  size_t ring;       /* fp8   [slots, 256, d] ring token buffer (ring dispatch only) */
+  size_t ring_s;     /* e8m0  [slots, 256, d/32] */
+  size_t ring_flags; /* int32 [2 slots + 1] */
+  size_t blkcnt;     /* int32 [ceil(T/64), E] per-block expert counts, then their scans */
+  size_t dyq;        /* fp8   [T, d]       dy quantised along d */
+  size_t dys;        /* e8m0  [T, d/32] */
+  size_t dw;         /* float [T, k]       gradient of the combine weights */
+  size_t dl;         /* float [T, k]       gradient of the selected logits */
+  size_t dguq;       /* fp8   [RS, 2I]     [dG dU] quantised along 2I (permuted rows) */
+  size_t dgus;       /* e8m0  [RS, 2I/32] */
+  size_t dxslot;     /* float [T, k + S, d] input gradient of every (token, slot) */
+  size_t xt;         /* fp8   [d, ld]      X rows of each expert, requantised along tokens */
+  size_t xts;        /* e8m0  [d, ld/32] */
+  size_t ht;         /* fp8   [I, ld]      H, same */
+  size_t hts;        /* e8m0  [I, ld/32] */
+  size_t dyt;        /* fp8   [d, ld]      w * dY, same */
+  size_t dyts;       /* e8m0  [d, ld/32] */
+  size_t dgut;       /* fp8   [2I, ld]     [dG dU], same */
+  size_t dguts;      /* e8m0  [2I, ld/32] */
+  size_t tok_stride; /* ld: tokens per row of the token-axis operands (a size, not an offset);
+                        expert e occupies columns [tok_off[e], tok_off[e + 1]) */
+  size_t total;      /* bytes of `workspace` */
+} moe_workspace_layout;
 
-/* MXFP8 quantisation of a [rows, cols] matrix along its contiguous axis (cols % 32 == 0):
+/* Sizes of the caller-owned buffers for `cfg`: *workspace_bytes for the workspace shared by
+ * moe_fwd and moe_bwd, *saved for the layout of the saved buffer (the schedule and activations
+ * the forward pass hands to the backward pass: knowledge card, 方法/产品要点, reusable schedule),
+ * *work for the layout of the workspace.  Any output pointer may be NULL.  Host-only; no GPU
+ * needed.  Returns MOE_ESHAPE / MOE_EINVAL for a configuration outside the supported set. */
+moe_status moe_query(const moe_config* cfg, size_t* workspace_bytes, moe_saved_layout* saved,
+                     moe_workspace_layout* work);
+
+/* MXFP8 quantisation (the format the pages name for the whole layer: knowledge card,
+ * 方法/产品要点, "MXFP8") of a [rows, cols] matrix along its contiguous axis (cols % 32 == 0):
  * src is bf16 (src_is_f32 = 0) or float32 (src_is_f32 = 1); q [rows, cols] fp8 and
  * scales [rows, cols/32] e8m0 receive the result.  Block scale 2^(floor(log2 amax) - 8), codes
- * rounded to nearest even and saturated at +-448 (the format the pages name: knowledge card,
- * 方法/产品要点, "MXFP8").  Used for expert weights and by the layer for x and dy. */
+ * rounded to nearest even and saturated at +-448.  Used for expert weights and by the layer for
+ * x and dy.  src and q 16-byte aligned.  Enqueued on `stream`; MOE_ESHAPE for cols % 32 != 0. */
 moe_status moe_quantize_mxfp8(const void* src, int src_is_f32, int64_t rows, int64_t cols, uint8_t* q,
                               uint8_t* scales, hipStream_t stream);
 
-/* Transposed requantisation: q [batch, rows, cols] fp8 with scales [batch, rows, cols/32]
- * (quantised along cols) is dequantised exactly and quantised again along rows into
- * qt [batch, cols, rows] with st [batch, cols, rows/32].  rows and cols multiples of 64.
- * This is the backward pass's requantisation of the expert weights (W1 along 2I, W2 along d),
- * which moe_bwd performs tile by tile inside its dgrad GEMMs with the same arithmetic; the
- * standalone form is exported for tests and for callers that want the transposed weights. */
+/* Transposed requantisation (the backward pass's requantisation of transposed operands, for an
+ * MXFP8 layer that also trains: knowledge card, 方法/产品要点, MXFP8 forward and backward):
+ * q [batch, rows, cols] fp8 with scales [batch, rows, cols/32] (quantised along cols) is
+ * dequantised exactly and quantised again along rows into qt [batch, cols, rows] with
+ * st [batch, cols, rows/32].  rows and cols multiples of 64 (else MOE_ESHAPE).  moe_fwd writes
+ * the expert weights' transposes (W1 along 2I, W2 along d) with the same arithmetic from its
+ * GEMMs' weight stream; this standalone form serves tests and callers that want them. */
 moe_status moe_requant_transpose(const uint8_t* q, const uint8_t* scales, int64_t batch, int64_t rows, int64_t cols,
                                  uint8_t* qt, uint8_t* st, hipStream_t stream);
 
-/* Forward pass.
+/* Forward pass of the layer (knowledge card, 方法/产品要点: DSV3-style MoE layer in MXFP8, pull-based
+ * forward dispatch, push-based forward combine, device-side schedule; commentary "Cursor 开源
+ * MoK…", section 什么是MoK: route, dispatch, expert FFN, combine).
  *   x [T, d] bf16; w_router [E, d] bf16; router_bias [E] float or NULL (added to every
  *   token's logits); w1q [NX, 2I, d] fp8 with w1s [NX, 2I, d/32] (gate rows 0..I-1, up rows
  *   I..2I-1, quantised along d); w2q [NX, d, I] fp8 with w2s [NX, d, I/32] (quantised along I).
  *   Outputs: y_bf16 [T, d]; y_f32 [T, d] float or NULL (the same sum before bf16 rounding);
- *   saved (moe_saved_layout) for moe_bwd.  workspace: moe_query's size.
+ *   saved (moe_saved_layout) for moe_bwd.  saved_bytes / workspace_bytes: the sizes of the
+ *   caller's buffers (MOE_EWORKSPACE if below what moe_query reports).
  * Steps (all on `stream`, no host sync): quantise x; router logits; top-k and weights; schedule
  * (counts, offsets, stable expert-major permutation); gate/up grouped GEMM with rows pulled
  * through the schedule, SwiGLU and H quantisation in the epilogue; down grouped GEMM pushing
- * each row to its (token, slot); combine in fixed slot order. */
+ * each row to its (token, slot); combine in fixed slot order.  Unless MOE_F_FORWARD_ONLY, the
+ * two GEMMs also requantise the weight slices they stream along the other axis into saved
+ * w1t / w2t, for the backward pass. */
 moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, const float* router_bias,
                    const uint8_t* w1q, const uint8_t* w1s, const uint8_t* w2q, const uint8_t* w2s, void* y_bf16,
-                   float* y_f32, void* saved, void* workspace, hipStream_t stream);
+                   float* y_f32, void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
 
 /* Backward pass for upstream gradient dy [T, d] bf16, reusing `saved` from moe_fwd of the same
- * inputs.  Outputs: dx_bf16 [T, d] and dx_f32 [T, d] float (or NULL); dw_router [E, d] float;
- * dw1 [NX, 2I, d] float and dw2 [NX, d, I] float (same layouts as w1q / w2q).
+ * inputs and configuration (knowledge card, 方法/产品要点: pull-based reverse-combine, push-based
+ * reverse-dispatch, schedule reused; article "Cursor 為 Composer 改造 MoE 訓練…", section
+ * "2.37 倍同 1.41 倍係兩份成績": the layer's backward).  The expert weights enter through their
+ * transposes in `saved`.  Outputs: dx_bf16 [T, d] and dx_f32 [T, d] float (or NULL);
+ * dw_router [E, d] float; dw1 [NX, 2I, d] float and dw2 [NX, d, I] float (same layouts as
+ * w1q / w2q).
  * Steps: quantise dy; combine-weight and router gradients; dgrad of the down GEMM (rows pulled
  * from dy: reverse-combine) with the SwiGLU backward and quantisation along 2I; dgrad of the
  * gate/up GEMM pushing rows to their (token, slot) (reverse-dispatch); fixed-order reduction of
- * dx; token-axis requantisation of the wgrad operands; weight-gradient GEMMs.  The two dgrad
- * GEMMs requantise their weight tiles along the contraction axis as they load them (W2 along d,
- * W1 along 2I: the transposed requantisation of the weights), so phase MOE_PH_REQUANT_W is
- * empty. */
-moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const void* w_router, const uint8_t* w1q,
-                   const uint8_t* w1s, const uint8_t* w2q, const uint8_t* w2s, const void* saved, void* dx_bf16,
-                   float* dx_f32, float* dw_router, float* dw1, float* dw2, void* workspace, hipStream_t stream);
+ * dx; token-axis requantisation of the wgrad operands; weight-gradient GEMMs. */
+moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const void* w_router, const void* saved,
+                   size_t saved_bytes, void* dx_bf16, float* dx_f32, float* dw_router, float* dw1, float* dw2,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Phase timing, for measurement only.  Phases of moe_fwd / moe_bwd, in launch order; the
- * library records events[p] on the call's stream right after phase p has been enqueued (and
- * events[MOE_PH_FWD_BEGIN] / events[MOE_PH_BWD_BEGIN] before the first launch), so the time
- * of phase p is the elapsed time between the previous recorded event and events[p].  Without
- * MOE_F_SERIAL_BWD the phases of the second-stream branch (MOE_PH_TOKEN_REQUANT's X / H / dY
- * part, MOE_PH_WGRAD_DOWN) overlap the others and their intervals do not measure them alone;
- * events[MOE_PH_WGRAD_DOWN] is then recorded after the join, so MOE_PH_WGRAD_GATEUP still
- * times dW1 alone.  The
- * caller creates the events (hipEventCreate) and keeps them alive; n_events = 0 turns timing
- * off.  Results are unaffected. */
+/* Phase timing, for measurement only (the pages attribute the layer's time to its phases:
+ * commentary "Cursor 开源 MoK…", section 瓶颈的真正来源).  Phases of moe_fwd / moe_bwd, in launch
+ * order; the library records events[p] on the call's stream right after phase p has been
+ * enqueued (and events[MOE_PH_FWD_BEGIN] / events[MOE_PH_BWD_BEGIN] before the first launch),
+ * so the time of phase p is the elapsed time between the previous recorded event and events[p].
+ * Without MOE_F_SERIAL_BWD the phases of the second-stream branch (MOE_PH_TOKEN_REQUANT's X / H /
+ * dY part, MOE_PH_WGRAD_DOWN) overlap the others and their intervals do not measure them alone;
+ * events[MOE_PH_WGRAD_DOWN] is then recorded after the join, so MOE_PH_WGRAD_GATEUP still times
+ * dW1 alone.  The caller creates the events (hipEventCreate) and keeps them alive; n_events = 0
+ * turns timing off.  Process-wide setting, not synchronised between threads.  Results are
+ * unaffected. */
 enum {
   MOE_PH_FWD_BEGIN = 0, MOE_PH_QUANT_X, MOE_PH_ROUTER, MOE_PH_TOPK, MOE_PH_SCHEDULE, MOE_PH_GATEUP,
   MOE_PH_DOWN, MOE_PH_COMBINE,
@@ -187,12 +252,13 @@ enum {
 };
 moe_status moe_set_phase_events(hipEvent_t* events, int32_t n_events);
 
-/* Reads the device status word of `workspace` (0 = fine) into *device_code.  Blocking copy:
- * call after the caller has synchronised the stream.  Returns MOE_EDEVICE if the code is
- * non-zero. */
+/* Reads the device status word of `workspace` (0 = fine; else a MOE_DEV_* code) into
+ * *device_code: the layer's way to report a device-side anomaly without a host sync inside the
+ * layer (knowledge card, 方法/产品要点: no CPU-GPU synchronisation).  Blocking copy: call after
+ * the caller has synchronised the stream.  Returns MOE_EDEVICE if the code is non-zero. */
 moe_status moe_device_status(const void* workspace, int32_t* device_code);
 
-/* Static text for a status. */
+/* Static text for a status (never NULL). */
 const char* moe_strerror(moe_status status);
 
 #ifdef __cplusplus

@@ -19,6 +19,8 @@ MOE_F_DIRECT_GATHER = 1
 MOE_F_RING_DISPATCH = 2
 MOE_F_SERIAL_BWD = 4
 MOE_F_IDENTITY_EXPERTS = 8
+MOE_F_FORWARD_ONLY = 16
+MOE_DEV_RING_TIMEOUT, MOE_DEV_NONFINITE_LOGIT = 1, 2
 
 # every symbol include/moe.h declares
 EXPORTS = ("moe_query", "moe_quantize_mxfp8", "moe_requant_transpose", "moe_fwd", "moe_bwd",
@@ -40,7 +42,13 @@ class moe_config(ctypes.Structure):
 class moe_saved_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "logits", "idx", "w", "counts", "offsets", "poffsets", "tok_off", "tile_start", "tile64", "perm", "pos",
-        "xq", "xs", "g", "u", "hq", "hs", "yslot", "total")]
+        "xq", "xs", "g", "u", "hq", "hs", "yslot", "w1t", "w1ts", "w2t", "w2ts", "total")]
+
+
+class moe_workspace_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "status", "ring", "ring_s", "ring_flags", "blkcnt", "dyq", "dys", "dw", "dl", "dguq", "dgus", "dxslot",
+        "xt", "xts", "ht", "hts", "dyt", "dyts", "dgut", "dguts", "tok_stride", "total")]
 
 
 class MoeError(RuntimeError):
@@ -61,11 +69,12 @@ def lib() -> ctypes.CDLL:
                               f"`python -m mixture_experts_layer_schedule_amd.build` (hipcc, gfx950)")
         L = ctypes.CDLL(LIB_PATH)
         P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
-        L.moe_query.argtypes = [ctypes.POINTER(moe_config), ctypes.POINTER(SZ), ctypes.POINTER(moe_saved_layout)]
+        L.moe_query.argtypes = [ctypes.POINTER(moe_config), ctypes.POINTER(SZ), ctypes.POINTER(moe_saved_layout),
+                                ctypes.POINTER(moe_workspace_layout)]
         L.moe_quantize_mxfp8.argtypes = [P, ctypes.c_int, I64, I64, P, P, P]
         L.moe_requant_transpose.argtypes = [P, P, I64, I64, I64, P, P, P]
-        L.moe_fwd.argtypes = [ctypes.POINTER(moe_config), P, P, P, P, P, P, P, P, P, P, P, P]
-        L.moe_bwd.argtypes = [ctypes.POINTER(moe_config), P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
+        L.moe_fwd.argtypes = [ctypes.POINTER(moe_config), P, P, P, P, P, P, P, P, P, P, SZ, P, SZ, P]
+        L.moe_bwd.argtypes = [ctypes.POINTER(moe_config), P, P, P, P, SZ, P, P, P, P, P, P, SZ, P]
         L.moe_set_phase_events.argtypes = [P, I32]
         L.moe_device_status.argtypes = [P, ctypes.POINTER(I32)]
         L.moe_strerror.argtypes = [ctypes.c_int]
@@ -109,11 +118,13 @@ def moe_strerror(status: int) -> str:
     return lib().moe_strerror(int(status)).decode()
 
 
-def moe_query(cfg: moe_config) -> tuple[int, moe_saved_layout]:
+def moe_query(cfg: moe_config, with_workspace_layout: bool = False):
+    """(workspace bytes, saved layout) or, with_workspace_layout, (bytes, saved layout, workspace layout)."""
     ws = ctypes.c_size_t(0)
     sl = moe_saved_layout()
-    _check(lib().moe_query(ctypes.byref(cfg), ctypes.byref(ws), ctypes.byref(sl)), "moe_query")
-    return ws.value, sl
+    wl = moe_workspace_layout()
+    _check(lib().moe_query(ctypes.byref(cfg), ctypes.byref(ws), ctypes.byref(sl), ctypes.byref(wl)), "moe_query")
+    return (ws.value, sl, wl) if with_workspace_layout else (ws.value, sl)
 
 
 def moe_quantize_mxfp8(src, src_is_f32: int, rows: int, cols: int, q, scales, stream=None) -> None:
@@ -126,18 +137,25 @@ def moe_requant_transpose(q, scales, batch: int, rows: int, cols: int, qt, st, s
                                        _stream(stream)), "moe_requant_transpose")
 
 
+def _nbytes(t, n) -> int:
+    """Byte size of a buffer: n if given, else the tensor's size."""
+    if n is not None:
+        return int(n)
+    return t.numel() * t.element_size()
+
+
 def moe_fwd(cfg, x, w_router, router_bias, w1q, w1s, w2q, w2s, y_bf16, y_f32, saved, workspace,
-            stream=None) -> None:
+            stream=None, saved_bytes=None, workspace_bytes=None) -> None:
     _check(lib().moe_fwd(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w1q), _ptr(w1s),
-                         _ptr(w2q), _ptr(w2s), _ptr(y_bf16), _ptr(y_f32), _ptr(saved), _ptr(workspace),
-                         _stream(stream)), "moe_fwd")
+                         _ptr(w2q), _ptr(w2s), _ptr(y_bf16), _ptr(y_f32), _ptr(saved), _nbytes(saved, saved_bytes),
+                         _ptr(workspace), _nbytes(workspace, workspace_bytes), _stream(stream)), "moe_fwd")
 
 
-def moe_bwd(cfg, dy, x, w_router, w1q, w1s, w2q, w2s, saved, dx_bf16, dx_f32, dw_router, dw1, dw2, workspace,
-            stream=None) -> None:
-    _check(lib().moe_bwd(ctypes.byref(cfg), _ptr(dy), _ptr(x), _ptr(w_router), _ptr(w1q), _ptr(w1s), _ptr(w2q),
-                         _ptr(w2s), _ptr(saved), _ptr(dx_bf16), _ptr(dx_f32), _ptr(dw_router), _ptr(dw1), _ptr(dw2),
-                         _ptr(workspace), _stream(stream)), "moe_bwd")
+def moe_bwd(cfg, dy, x, w_router, saved, dx_bf16, dx_f32, dw_router, dw1, dw2, workspace, stream=None,
+            saved_bytes=None, workspace_bytes=None) -> None:
+    _check(lib().moe_bwd(ctypes.byref(cfg), _ptr(dy), _ptr(x), _ptr(w_router), _ptr(saved),
+                         _nbytes(saved, saved_bytes), _ptr(dx_bf16), _ptr(dx_f32), _ptr(dw_router), _ptr(dw1),
+                         _ptr(dw2), _ptr(workspace), _nbytes(workspace, workspace_bytes), _stream(stream)), "moe_bwd")
 
 
 def moe_set_phase_events(events, n_events: int) -> None:

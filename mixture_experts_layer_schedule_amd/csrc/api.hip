@@ -33,11 +33,15 @@ Dims dims(const moe_config& c) {
   m.ld_tok = (int64_t)up((size_t)(m.RS + 127 * m.NX), 128);
   m.tiles_bound = m.RS / 256 + m.NX + 1;  // sum over experts of ceil(count / 256)
   m.tile64_bound = m.ld_tok / 64;
-  const int64_t ring_rows = c.ring_rows ? c.ring_rows : kDefaultRingRows;
+  // the ring buffer exists only for the ring dispatch
+  const int64_t ring_rows = !(c.flags & MOE_F_RING_DISPATCH) ? 0 : c.ring_rows ? c.ring_rows : kDefaultRingRows;
   m.nslots = ring_rows / kChunkRows;
   m.producers = c.producer_wgs ? c.producer_wgs : kDefaultProducers;
   return m;
 }
+
+constexpr uint32_t kKnownFlags =
+    MOE_F_DIRECT_GATHER | MOE_F_RING_DISPATCH | MOE_F_SERIAL_BWD | MOE_F_IDENTITY_EXPERTS | MOE_F_FORWARD_ONLY;
 
 moe_status check_config(const moe_config* c) {
   if (!c) return MOE_EINVAL;
@@ -45,14 +49,22 @@ moe_status check_config(const moe_config* c) {
   if (c->k < 1 || c->k > 16 || c->E < c->k || c->E > 512) return MOE_ESHAPE;
   if (c->n_shared < 0 || c->n_shared > 1) return MOE_ESHAPE;
   if (c->score_fn != MOE_SCORE_SOFTMAX && c->score_fn != MOE_SCORE_SIGMOID) return MOE_EINVAL;
+  if (c->flags & ~kKnownFlags) return MOE_EINVAL;
+  if ((c->flags & MOE_F_DIRECT_GATHER) && (c->flags & MOE_F_RING_DISPATCH)) return MOE_EINVAL;
+  if (c->flags & MOE_F_RING_DISPATCH) return MOE_EINVAL;  // disabled: see the ring kernel's header
+  // the tuning knobs only act on the ring dispatch
+  if (!(c->flags & MOE_F_RING_DISPATCH) && (c->ring_rows || c->chunk_rows || c->producer_wgs)) return MOE_EINVAL;
   if (c->ring_rows < 0 || c->producer_wgs < 0 || c->producer_wgs > 128) return MOE_ESHAPE;
   if (c->ring_rows && (c->ring_rows < kChunkRows || c->ring_rows % kChunkRows)) return MOE_ESHAPE;
   if (c->chunk_rows != 0 && c->chunk_rows != kChunkRows) return MOE_ESHAPE;
-  if (c->flags & ~(MOE_F_DIRECT_GATHER | MOE_F_RING_DISPATCH | MOE_F_SERIAL_BWD | MOE_F_IDENTITY_EXPERTS))
-    return MOE_EINVAL;
-  if ((c->flags & MOE_F_DIRECT_GATHER) && (c->flags & MOE_F_RING_DISPATCH)) return MOE_EINVAL;
-  if (c->flags & MOE_F_RING_DISPATCH) return MOE_EINVAL;  // disabled: see the ring kernel's header
-  if ((int64_t)c->T * c->k + (int64_t)c->n_shared * c->T >= (1ll << 30)) return MOE_ESHAPE;
+  const int64_t RS = (int64_t)c->T * c->k + (int64_t)c->n_shared * c->T;
+  if (RS >= (1ll << 30)) return MOE_ESHAPE;
+  // operands addressed with 32-bit byte offsets from one base: the gathered activations
+  // (xq, dyq: T*d), one expert's weights (2I*d) and the token-axis operands of the weight
+  // gradients (up to 256 rows of stride ld_tok)
+  if ((int64_t)c->T * c->d >= (1ll << 32)) return MOE_ESHAPE;
+  if (2 * (int64_t)c->inter * c->d >= (1ll << 32)) return MOE_ESHAPE;
+  if (dims(*c).ld_tok >= (1ll << 24)) return MOE_ESHAPE;
   return MOE_OK;
 }
 
@@ -66,7 +78,7 @@ struct Layout {
   }
 };
 
-moe_saved_layout saved_layout(const Dims& m) {
+moe_saved_layout saved_layout(const Dims& m, uint32_t flags) {
   moe_saved_layout s{};
   Layout L;
   s.logits = L.take(4 * m.T * m.E);
@@ -87,17 +99,18 @@ moe_saved_layout saved_layout(const Dims& m) {
   s.hq = L.take(m.RS * m.I);
   s.hs = L.take(m.RS * m.I / 32);
   s.yslot = L.take(4 * m.T * (m.k + m.S) * m.d);
+  const bool wt = !(flags & (MOE_F_FORWARD_ONLY | MOE_F_IDENTITY_EXPERTS));
+  const size_t wbytes = wt ? (size_t)(m.NX * 2 * m.I * m.d) : 0;
+  s.w1t = L.take(wbytes);
+  s.w1ts = L.take(wbytes / 32);
+  s.w2t = L.take(wbytes / 2);
+  s.w2ts = L.take(wbytes / 64);
   s.total = L.off;
   return s;
 }
 
-struct Work {
-  size_t status, ring, ring_s, ring_flags, blkcnt, dyq, dys, dw, dl, dguq, dgus, dxslot;
-  size_t xt, xts, ht, hts, dyt, dyts, dgut, dguts, total;
-};
-
-Work work_layout(const Dims& m) {
-  Work w{};
+moe_workspace_layout work_layout(const Dims& m) {
+  moe_workspace_layout w{};
   Layout L;
   w.status = L.take(64);
   w.ring = L.take(m.nslots * kChunkRows * m.d);
@@ -119,6 +132,7 @@ Work work_layout(const Dims& m) {
   w.dyts = L.take(m.d * m.ld_tok / 32);
   w.dgut = L.take(2 * m.I * m.ld_tok);
   w.dguts = L.take(2 * m.I * m.ld_tok / 32);
+  w.tok_stride = (size_t)m.ld_tok;
   w.total = L.off;
   return w;
 }
@@ -149,22 +163,21 @@ moe_status ensure_init() {
   return g_init_err == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }
 
-// Second stream of each device for the backward's independent branch (created on first use,
-// default priority, kept until the process ends) and the fork / join events around it.
+// Second stream of each device for the backward's independent branch, with the fork / join
+// events around it: one set per host thread and device (created on first use, default
+// priority, kept until the process ends), so calls from different threads never share events.
 struct SideStream {
   hipStream_t st = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
   bool ok = false, tried = false;
 };
 constexpr int kMaxDevices = 64;
-SideStream g_side[kMaxDevices];
-std::mutex g_side_mu;
+thread_local SideStream t_side[kMaxDevices];
 
 SideStream* side_stream() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  std::lock_guard<std::mutex> lk(g_side_mu);
-  SideStream& s = g_side[dev];
+  SideStream& s = t_side[dev];
   if (!s.tried) {
     s.tried = true;
     s.ok = hipStreamCreateWithFlags(&s.st, hipStreamNonBlocking) == hipSuccess &&
@@ -196,12 +209,15 @@ SchedView sched_view(const void* saved, const moe_saved_layout& sl, const Dims& 
 
 extern "C" {
 
-moe_status moe_query(const moe_config* cfg, size_t* workspace_bytes, moe_saved_layout* saved) {
+moe_status moe_query(const moe_config* cfg, size_t* workspace_bytes, moe_saved_layout* saved,
+                     moe_workspace_layout* work) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
   Dims m = dims(*cfg);
-  if (workspace_bytes) *workspace_bytes = work_layout(m).total;
-  if (saved) *saved = saved_layout(m);
+  const moe_workspace_layout wl = work_layout(m);
+  if (workspace_bytes) *workspace_bytes = wl.total;
+  if (saved) *saved = saved_layout(m, cfg->flags);
+  if (work) *work = wl;
   return MOE_OK;
 }
 
@@ -224,24 +240,28 @@ moe_status moe_requant_transpose(const uint8_t* q, const uint8_t* scales, int64_
 
 moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, const float* router_bias,
                    const uint8_t* w1q, const uint8_t* w1s, const uint8_t* w2q, const uint8_t* w2s, void* y_bf16,
-                   float* y_f32, void* saved, void* workspace, hipStream_t stream) {
+                   float* y_f32, void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
   if (!x || !w_router || !w1q || !w1s || !w2q || !w2s || !y_bf16 || !saved || !workspace) return MOE_EINVAL;
   if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(w1q, 16) || !aligned(w2q, 16) || !aligned(y_bf16, 16) ||
       (y_f32 && !aligned(y_f32, 16)) || !aligned(saved, kAlign) || !aligned(workspace, kAlign))
     return MOE_EALIGN;
-  if ((st = ensure_init()) != MOE_OK) return st;
   const Dims m = dims(*cfg);
-  const moe_saved_layout sl = saved_layout(m);
-  const Work wl = work_layout(m);
+  const moe_saved_layout sl = saved_layout(m, cfg->flags);
+  const moe_workspace_layout wl = work_layout(m);
+  if (saved_bytes < sl.total || workspace_bytes < wl.total) return MOE_EWORKSPACE;
+  if ((st = ensure_init()) != MOE_OK) return st;
   const int d = (int)m.d, I = (int)m.I;
+  const bool want_wt = !(cfg->flags & MOE_F_FORWARD_ONLY);
 
   uint8_t* xq = at<uint8_t>(saved, sl.xq);
   uint8_t* xs = at<uint8_t>(saved, sl.xs);
   float* logits = at<float>(saved, sl.logits);
   int32_t* idx = at<int32_t>(saved, sl.idx);
   float* w = at<float>(saved, sl.w);
+  int32_t* status = at<int32_t>(workspace, wl.status);
 
   mark(stream, MOE_PH_FWD_BEGIN);
   MOE_TRY(launch_quant_rows(x, 0, m.T, m.d, xq, xs, stream));
@@ -249,7 +269,7 @@ moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, c
   MOE_TRY(launch_router_logits((const uint16_t*)x, (const uint16_t*)w_router, router_bias, logits, (int)m.T, d,
                                (int)m.E, stream));
   mark(stream, MOE_PH_ROUTER);
-  MOE_TRY(launch_topk(logits, (int)m.T, (int)m.E, (int)m.k, cfg->score_fn, idx, w, stream));
+  MOE_TRY(launch_topk(logits, (int)m.T, (int)m.E, (int)m.k, cfg->score_fn, idx, w, status, stream));
 
   SchedBuild sb;
   sb.idx = idx;
@@ -291,6 +311,8 @@ moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, c
   ga.u = at<float>(saved, sl.u);
   ga.hq = at<uint8_t>(saved, sl.hq);
   ga.hs = at<uint8_t>(saved, sl.hs);
+  ga.w1t = want_wt ? at<uint8_t>(saved, sl.w1t) : nullptr;
+  ga.w1ts = want_wt ? at<uint8_t>(saved, sl.w1ts) : nullptr;
   ga.d = d;
   ga.I = I;
   if (!(cfg->flags & MOE_F_RING_DISPATCH)) {
@@ -314,7 +336,7 @@ moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, c
     ra.ready = ra.flags;
     ra.done = ra.flags + m.nslots;
     ra.abort_flag = ra.flags + 2 * m.nslots;
-    ra.status = at<int32_t>(workspace, wl.status);
+    ra.status = status;
     ra.d = d;
     ra.I = I;
     ra.nslots = (int)m.nslots;
@@ -331,6 +353,8 @@ moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, c
   da.w2q = w2q;
   da.w2s = w2s;
   da.yslot = at<float>(saved, sl.yslot);
+  da.w2t = want_wt ? at<uint8_t>(saved, sl.w2t) : nullptr;
+  da.w2ts = want_wt ? at<uint8_t>(saved, sl.w2ts) : nullptr;
   da.d = d;
   da.I = I;
   MOE_TRY(launch_gemm_down(da, (int)m.tiles_bound, stream));
@@ -341,23 +365,23 @@ moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, c
   return MOE_OK;
 }
 
-moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const void* w_router, const uint8_t* w1q,
-                   const uint8_t* w1s, const uint8_t* w2q, const uint8_t* w2s, const void* saved, void* dx_bf16,
-                   float* dx_f32, float* dw_router, float* dw1, float* dw2, void* workspace, hipStream_t stream) {
+moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const void* w_router, const void* saved,
+                   size_t saved_bytes, void* dx_bf16, float* dx_f32, float* dw_router, float* dw1, float* dw2,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
-  if (cfg->flags & MOE_F_IDENTITY_EXPERTS) return MOE_EINVAL;  // forward-only check mode
-  if (!dy || !x || !w_router || !w1q || !w1s || !w2q || !w2s || !saved || !dx_bf16 || !dw_router || !dw1 || !dw2 ||
-      !workspace)
-    return MOE_EINVAL;
-  if (!aligned(dy, 16) || !aligned(x, 16) || !aligned(w_router, 16) || !aligned(w1q, 16) || !aligned(w2q, 16) ||
-      !aligned(dx_bf16, 16) || (dx_f32 && !aligned(dx_f32, 16)) || !aligned(dw_router, 16) || !aligned(dw1, 16) ||
-      !aligned(dw2, 16) || !aligned(saved, kAlign) || !aligned(workspace, kAlign))
+  // forward-only check mode / forward-only layout: there is no saved state to differentiate
+  if (cfg->flags & (MOE_F_IDENTITY_EXPERTS | MOE_F_FORWARD_ONLY)) return MOE_EINVAL;
+  if (!dy || !x || !w_router || !saved || !dx_bf16 || !dw_router || !dw1 || !dw2 || !workspace) return MOE_EINVAL;
+  if (!aligned(dy, 16) || !aligned(x, 16) || !aligned(w_router, 16) || !aligned(dx_bf16, 16) ||
+      (dx_f32 && !aligned(dx_f32, 16)) || !aligned(dw_router, 16) || !aligned(dw1, 16) || !aligned(dw2, 16) ||
+      !aligned(saved, kAlign) || !aligned(workspace, kAlign))
     return MOE_EALIGN;
-  if ((st = ensure_init()) != MOE_OK) return st;
   const Dims m = dims(*cfg);
-  const moe_saved_layout sl = saved_layout(m);
-  const Work wl = work_layout(m);
+  const moe_saved_layout sl = saved_layout(m, cfg->flags);
+  const moe_workspace_layout wl = work_layout(m);
+  if (saved_bytes < sl.total || workspace_bytes < wl.total) return MOE_EWORKSPACE;
+  if ((st = ensure_init()) != MOE_OK) return st;
   const int d = (int)m.d, I = (int)m.I;
   const SchedView sv = sched_view(saved, sl, m);
   const float* w = at<float>(saved, sl.w);
@@ -423,16 +447,17 @@ moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const v
   MOE_TRY(launch_router_wgrad(sv, dl, (const uint16_t*)x, d, (int)m.E, dw_router, stream));
   mark(stream, MOE_PH_ROUTER_WGRAD);
 
-  // The transposed requantisation of the expert weights (W1 along 2I, W2 along d) happens inside
-  // the two dgrad GEMMs, tile by tile, from w1q / w2q: the phase below is empty.
+  // The transposed requantisation of the expert weights (W1 along 2I, W2 along d) was done by
+  // the forward GEMMs from the weight slices they streamed (saved w1t / w2t): the phase below
+  // is empty.
   mark(stream, MOE_PH_REQUANT_W);
 
   DgradDownArgs dd;
   dd.s = sv;
   dd.dyq = dyq;
   dd.dys = dys;
-  dd.w2q = w2q;
-  dd.w2s = w2s;
+  dd.w2t = at<uint8_t>(saved, sl.w2t);
+  dd.w2ts = at<uint8_t>(saved, sl.w2ts);
   dd.w = w;
   dd.g = at<float>(saved, sl.g);
   dd.u = at<float>(saved, sl.u);
@@ -447,8 +472,8 @@ moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const v
   dg.s = sv;
   dg.dguq = dd.dguq;
   dg.dgus = dd.dgus;
-  dg.w1q = w1q;
-  dg.w1s = w1s;
+  dg.w1t = at<uint8_t>(saved, sl.w1t);
+  dg.w1ts = at<uint8_t>(saved, sl.w1ts);
   dg.dxslot = at<float>(workspace, wl.dxslot);
   dg.d = d;
   dg.I = I;

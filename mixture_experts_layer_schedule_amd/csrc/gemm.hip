@@ -2,6 +2,11 @@
 // in gemm_core.h.  The routed GEMMs run one (row tile, 256-column tile) item per workgroup; the
 // row count of the item picks the instantiation with that many 32-row fragments.  The forward
 // GEMMs run the tile with 8 waves (two per SIMD, 512 threads), the backward ones with 4.
+//
+// The forward GEMMs also produce the transposed, requantised weights the backward pass
+// contracts with (W1 along 2I, W2 along d): each stage's staged weight slice is requantised
+// along its rows by one of the row tiles that share it (stage t by row tile t % nm), so every
+// weight element of an expert with rows is requantised exactly once per forward pass.
 #include "common.h"
 #include "gemm_core.h"
 #include "kernels.h"
@@ -56,6 +61,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_gateup(GateUpArgs p) {
   const uint8_t* w1 = p.w1q + (size_t)rt.e * 2 * I * d;
   const uint8_t* w1s = p.w1s + (size_t)rt.e * 2 * I * (d / 32);
   const int last = rt.rows - 1;
+  // transposed weight W1t[e] [d][2I]: staged row block w (32 rows) holds gate rows
+  // n0 + 32(w / 2) .. (w even) or the matching up rows (w odd)
+  const int wv = threadIdx.x >> 6;
+  uint8_t* w1t = p.w1t ? p.w1t + (size_t)rt.e * d * 2 * I : nullptr;
+  uint8_t* w1ts = p.w1t ? p.w1ts + (size_t)rt.e * d * (2 * I / 32) : nullptr;
+  const int orow = (wv & 1 ? I : 0) + n0 + 32 * (wv >> 1);
+  auto after = [=](const uint8_t* st, int t) __attribute__((always_inline)) {
+    if (w1t && t % rt.nm == rt.m) requant_stage_t8(st, t * KS, orow, w1t, w1ts, 2 * I);
+  };
   dispatch_rows(rt.rows, [&]<int F>() {
     TileLoads8<F> L;
     L.init(p.xq, [&](int r) { return p.xq + (size_t)row_token(s, rt.r0 + min(r, last)) * d; },
@@ -63,7 +77,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_gateup(GateUpArgs p) {
            p.xs, [&](int r) { return p.xs + (size_t)row_token(s, rt.r0 + min(r, last)) * (d / 32); },
            w1s, [&](int r) { return w1s + (size_t)gateup_brow(r, n0, I) * (d / 32); });
     v16f acc[(F + 1) / 2][2];
-    mainloop8<F>(lds, L, d / KS, acc);
+    mainloop8<F>(lds, L, d / KS, acc, after);
     gateup_epilogue8<F>(acc, rt.r0, rt.rows, n0, I, p.g, p.u, p.hq, p.hs);
   });
 }
@@ -86,6 +100,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_down(DownArgs p) {
   const int last = rt.rows - 1;
   const int w = threadIdx.x >> 6, l = lane_id(), i = l & 31, h = l >> 5, wc = w & 3;
   const bool active = n0 + 64 * wc < d;
+  // transposed weight W2t[e] [I][d]: staged row block w holds W2 rows n0 + 32w .. (none past d)
+  uint8_t* w2t = p.w2t ? p.w2t + (size_t)rt.e * I * d : nullptr;
+  uint8_t* w2ts = p.w2t ? p.w2ts + (size_t)rt.e * I * (d / 32) : nullptr;
+  const int orow = n0 + 32 * w < d ? n0 + 32 * w : -1;
+  auto after = [=](const uint8_t* st, int t) __attribute__((always_inline)) {
+    if (w2t && t % rt.nm == rt.m) requant_stage_t8(st, t * KS, orow, w2t, w2ts, d);
+  };
   dispatch_rows(rt.rows, [&]<int F>() {
     constexpr int FH = (F + 1) / 2;
     const int m0 = (w >> 2) * FH;
@@ -97,7 +118,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_down(DownArgs p) {
            hsa, [&](int r) { return hsa + (size_t)min(r, last) * (I / 32); },
            w2s, [&](int r) { return w2s + (size_t)min(n0 + r, d - 1) * (I / 32); });
     v16f acc[FH][2];
-    mainloop8<F>(lds, L, I / KS, acc);
+    mainloop8<F>(lds, L, I / KS, acc, after);
     const int64_t* slot = row_slot_table(s, rt, lds + ((I / KS) % kStages) * STAGE_BYTES);
     if (!active) return;
     static_for<FH>([&]<int m>() {
@@ -131,16 +152,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_down(DgradDownArgs p) {
   const int last = rt.rows - 1;
   const int w = threadIdx.x >> 6, l = lane_id(), i = l & 31, h = l >> 5;
   const bool active = n0 + 64 * w < I;
+  const uint8_t* w2t = p.w2t + (size_t)rt.e * I * d;  // W2^T [I][d], quantised along d
+  const uint8_t* w2ts = p.w2ts + (size_t)rt.e * I * (d / 32);
   dispatch_rows(rt.rows, [&]<int F>() {
     TileLoads<F> L;
     L.init(p.dyq, [&](int r) { return p.dyq + (size_t)row_token(s, rt.r0 + min(r, last)) * d; },
-           p.dyq, [&](int) { return p.dyq; },
+           w2t, [&](int r) { return w2t + (size_t)min(n0 + r, I - 1) * d; },
            p.dys, [&](int r) { return p.dys + (size_t)row_token(s, rt.r0 + min(r, last)) * (d / 32); },
-           p.dys, [&](int) { return p.dys; });
-    TransB tb;  // W2t = W2^T requantised along d: K = d rows of W2, N = I columns
-    tb.init(p.w2q + (size_t)rt.e * d * I, p.w2s + (size_t)rt.e * d * (I / 32), I, n0);
+           w2ts, [&](int r) { return w2ts + (size_t)min(n0 + r, I - 1) * (d / 32); });
     v16f acc[F][2];
-    mainloop_tb<F>(lds, L, tb, d / KS, acc);
+    mainloop<F, 2>(lds, L, d / KS, acc);
     // combine weight of every row of the tile, once, through LDS
     float* wt = (float*)(lds + ((d / KS) % kStages) * STAGE_BYTES);
     if ((int)threadIdx.x < rt.rows) wt[threadIdx.x] = row_weight(s, p.w, rt.r0 + threadIdx.x);
@@ -205,18 +226,18 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_gateup(DgradGateUpArgs p)
   const int last = rt.rows - 1;
   const int w = threadIdx.x >> 6, l = lane_id(), i = l & 31, h = l >> 5;
   const bool active = n0 + 64 * w < d;
+  const uint8_t* w1t = p.w1t + (size_t)rt.e * d * I2;  // W1^T [d][2I], quantised along 2I
+  const uint8_t* w1ts = p.w1ts + (size_t)rt.e * d * (I2 / 32);
   dispatch_rows(rt.rows, [&]<int F>() {
     TileLoads<F> L;
     const uint8_t* ga = p.dguq + (size_t)rt.r0 * I2;
     const uint8_t* gsa = p.dgus + (size_t)rt.r0 * (I2 / 32);
     L.init(ga, [&](int r) { return ga + (size_t)min(r, last) * I2; },
-           ga, [&](int) { return ga; },
+           w1t, [&](int r) { return w1t + (size_t)min(n0 + r, d - 1) * I2; },
            gsa, [&](int r) { return gsa + (size_t)min(r, last) * (I2 / 32); },
-           gsa, [&](int) { return gsa; });
-    TransB tb;  // W1t = W1^T requantised along 2I: K = 2I rows of W1, N = d columns
-    tb.init(p.w1q + (size_t)rt.e * I2 * d, p.w1s + (size_t)rt.e * I2 * (d / 32), d, n0);
+           w1ts, [&](int r) { return w1ts + (size_t)min(n0 + r, d - 1) * (I2 / 32); });
     v16f acc[F][2];
-    mainloop_tb<F>(lds, L, tb, I2 / KS, acc);
+    mainloop<F, 2>(lds, L, I2 / KS, acc);
     const int64_t* slot = row_slot_table(s, rt, lds + ((I2 / KS) % kStages) * STAGE_BYTES);
     if (!active) return;
     static_for<F>([&]<int mi>() {

@@ -28,6 +28,8 @@
 // Each output tile is owned by exactly one workgroup and K is summed in a fixed order, so
 // results are bitwise reproducible.
 #pragma once
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -68,16 +70,17 @@ MOE_DEV int tile_expert(const int32_t* tile_start, int n_exp, int tile) {
 // 256 accumulator registers per lane.)
 struct RowTile {
   int e, r0, rows;
+  int m, nm;  // index of the tile among the expert's nm row tiles
 };
 MOE_DEV RowTile row_tile(const SchedView& s, int tile) {
   RowTile t;
   t.e = tile_expert(s.tile_start, s.n_exp, tile);
-  const int m = tile - s.tile_start[t.e];
-  const int nm = s.tile_start[t.e + 1] - s.tile_start[t.e];
+  t.m = tile - s.tile_start[t.e];
+  t.nm = s.tile_start[t.e + 1] - s.tile_start[t.e];
   const int c = s.offsets[t.e + 1] - s.offsets[t.e];
-  const int per = ((c + nm - 1) / nm + 31) & ~31;
-  t.r0 = s.offsets[t.e] + m * per;
-  t.rows = min(per, c - m * per);
+  const int per = ((c + t.nm - 1) / t.nm + 31) & ~31;
+  t.r0 = s.offsets[t.e] + t.m * per;
+  t.rows = min(per, c - t.m * per);
   return t;
 }
 
@@ -213,8 +216,8 @@ MOE_DEV void pin_agprs(v16f& a, v16f& b) { asm volatile("" : "+a"(a), "+a"(b)::"
 // read two at a time, one pair ahead of the matrix instructions that use the previous pair
 // (scheduling barriers keep that order): LDS returns in order, so each instruction waits only
 // for its own operands while the next pair is arriving, and few registers hold fragments.
-template <int F, class Hook>
-MOE_DEV void compute_stage(const uint8_t* st, v16f (&acc)[F][2], const Hook& hook) {
+template <int F>
+MOE_DEV void compute_stage(const uint8_t* st, v16f (&acc)[F][2]) {
   const int l = lane_id(), i = l & 31, h = l >> 5, w = threadIdx.x >> 6;
   const int sw = swz(i);
   const uint32_t* sc = (const uint32_t*)(st + DATA_BYTES);
@@ -251,30 +254,9 @@ MOE_DEV void compute_stage(const uint8_t* st, v16f (&acc)[F][2], const Hook& hoo
                                                                         sb[1] >> (16 * kk));
         }
       });
-      // independent vector work placed here issues while the matrix core runs the group
-      if constexpr (!Hook::kEmpty) {
-        hook.template operator()<kk * NG + g, 2 * NG>();
-        // interleave: one matrix instruction, then a share of the hook's vector work, so the
-        // vector work issues while the matrix core runs
-        constexpr int NM = 2 * ((2 * g + 1 < F) ? 2 : 1);
-        static_for<NM>([&]<int x>() {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 28, 0);
-        });
-      }
       __builtin_amdgcn_sched_barrier(0);
     });
   });
-}
-
-struct NoHook {
-  static constexpr bool kEmpty = true;
-  template <int G, int NGROUPS>
-  MOE_DEV void operator()() const {}
-};
-template <int F>
-MOE_DEV void compute_stage(const uint8_t* st, v16f (&acc)[F][2]) {
-  compute_stage<F>(st, acc, NoHook{});
 }
 
 // acc = A_tile * B_tile^T over K = 128 * nk.  Every wave multiplies, also one whose columns lie
@@ -293,146 +275,6 @@ MOE_DEV void mainloop(uint8_t* lds, const TileLoads<F>& L, int nk, v16f (&acc)[F
     wait_loads_and_sync<0>();  // stage t has landed; every wave is done with stage t - 1
     if (t + 1 < nk) issue_stage<F, NST, AUX_A>(L, lds, t + 1);
     compute_stage<F>(lds + (t % NST) * STAGE_BYTES, acc);
-  }
-}
-
-// B operand of a dgrad GEMM built in the kernel from a forward weight ("transposed
-// requantisation").  The forward weight Wq of one expert is a K x N code matrix quantised along
-// its rows (blocks of 32 of the N values); the dgrad GEMM contracts over K, so its B tile (N
-// rows, K contiguous, blocks along K) is W^T requantised: every 32 K values of a column are
-// dequantised exactly (e4m3 code x 2^(e - 127) is a float32) and quantised again with the
-// block's own e8m0 exponent, the arithmetic of the standalone requantisation kernel.  Doing it
-// here reads the weight once per tile instead of writing and re-reading a transposed copy.
-//
-// Stage t covers K rows [128t, 128t + 128): wave w requantises K block w (32 rows) of the 256
-// tile columns; lane l holds columns [16 (l % 16), +16) of rows 8 (l / 16) .. +8 of that block,
-// loaded as eight 16-byte pieces (four lanes of a wave instruction share a row, so one
-// instruction reads four whole 256-byte row segments) plus one scale byte per row.  The block
-// maximum of a column spans the four lanes l, l ^ 16, l ^ 32, l ^ 48.  Each column's 8 new codes
-// go to the staged B row as one 8-byte LDS write and its new scale byte to the stage's B scale
-// word (byte w = K block w).
-struct TransB {
-  const uint8_t* q;  // [K][N] codes of the expert
-  const uint8_t* s;  // [K][N / 32] scale bytes
-  int N;
-  uint32_t qoff, soff;  // this lane's first piece / scale byte (K row 32w + 8(l / 16), stage 0)
-  v4i raw[8];           // the stage being requantised: 8 row pieces,
-  float f[8];           // their dequantisation factors 2^(e - 127)
-  v4i nraw[8];          // the next stage, in flight: pieces and scale bytes
-  uint32_t nsraw[8];
-
-  // n0: first column of the tile; columns past N (N a multiple of 128) repeat the last valid
-  // 16 (their results are dropped).
-  MOE_DEV void init(const uint8_t* q_, const uint8_t* s_, int N_, int n0) {
-    q = q_; s = s_; N = N_;
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int col = min(n0 + 16 * (l & 15), N - 16);
-    const int row = 32 * w + 8 * (l >> 4);
-    qoff = (uint32_t)row * (uint32_t)N + (uint32_t)col;
-    soff = (uint32_t)row * (uint32_t)(N / 32) + (uint32_t)(col >> 5);
-  }
-
-  // 16 loads per lane into the in-flight set: 8 pieces, then 8 scale bytes.
-  MOE_DEV void load_next(int t) {
-    const uint32_t r0 = (uint32_t)(128 * t);
-    static_for<8>([&]<int j>() { nraw[j] = *(const v4i*)(q + (qoff + (r0 + j) * (uint32_t)N)); });
-    static_for<8>([&]<int j>() { nsraw[j] = s[soff + (r0 + j) * (uint32_t)(N / 32)]; });
-  }
-
-  // The in-flight stage becomes the one to requantise (waits for its loads).  (Two register
-  // sets alternating by stage parity would save these copies, but the two-stage loop body that
-  // needs makes the kernel spill.)
-  MOE_DEV void advance() {
-    static_for<8>([&]<int j>() {
-      raw[j] = nraw[j];
-      f[j] = e8m0_scale(nsraw[j]);
-    });
-  }
-
-  // Requantise column pair P of this lane (word P / 2 of every piece, half P % 2: columns
-  // 16 (l % 16) + 2P, + 1) into stage buffer st.
-  template <int P>
-  MOE_DEV void requant_pair(uint8_t* st) const {
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int cg = l & 15, ng = l >> 4;
-    float v[8][2];
-    static_for<8>([&]<int j>() {
-      const v2f x = __builtin_amdgcn_cvt_pk_f32_fp8(raw[j][P >> 1], (P & 1) != 0);
-      v[j][0] = x[0] * f[j];
-      v[j][1] = x[1] * f[j];
-    });
-    static_for<2>([&]<int c>() {
-      float m = 0.0f;
-      static_for<8>([&]<int j>() { m = fmaxf(m, fabsf(v[j][c])); });
-      // maximum over the lanes l ^ 16, l ^ 32, l ^ 48 (the other 24 rows of the block); the
-      // maxima are non-negative, so they are compared as integers (no canonicalisation)
-      uint32_t mu = __float_as_uint(m);
-      const auto p16 = __builtin_amdgcn_permlane16_swap((int)mu, (int)mu, false, false);
-      mu = max((uint32_t)p16[0], (uint32_t)p16[1]);
-      const auto p32 = __builtin_amdgcn_permlane32_swap((int)mu, (int)mu, false, false);
-      mu = max((uint32_t)p32[0], (uint32_t)p32[1]);
-      const uint32_t byte = e8m0_from_amax(__uint_as_float(mu));
-      const float inv = e8m0_inv_scale(byte);
-      v2i codes;
-      codes[0] = (int)pack4_e4m3(v[0][c] * inv, v[1][c] * inv, v[2][c] * inv, v[3][c] * inv);
-      codes[1] = (int)pack4_e4m3(v[4][c] * inv, v[5][c] * inv, v[6][c] * inv, v[7][c] * inv);
-      const int r = 16 * cg + 2 * P + c;  // staged B row = tile column
-      const int chunk = 2 * w + (ng >> 1);
-      *(v2i*)(st + A_STAGE + r * KS + 16 * (chunk ^ swz(r)) + 8 * (ng & 1)) = codes;
-      st[DATA_BYTES + TM * 4 + 4 * r + w] = (uint8_t)byte;  // the 4 lanes of a column write the same byte
-    });
-  }
-
-  template <int P0, int P1>
-  MOE_DEV void requant_pairs(uint8_t* st) const {
-    static_for<P1 - P0>([&]<int p>() { requant_pair<P0 + p>(st); });
-  }
-};
-
-// Spreads the requantisation of the next stage (8 column pairs per lane) over the matrix
-// groups of compute_stage, so that its vector work issues while the matrix core is busy.  No
-// branch: a branch between the groups would let the compiler gather every fragment read ahead
-// of the matrix instructions.
-struct RequantHook {
-  static constexpr bool kEmpty = false;
-  const TransB& tb;
-  uint8_t* st;
-  template <int G, int NGROUPS>
-  MOE_DEV void operator()() const {
-    tb.requant_pairs<8 * G / NGROUPS, 8 * (G + 1) / NGROUPS>(st);
-  }
-};
-
-// mainloop with the B tile requantised in the kernel from a forward weight (TransB).  Stage t:
-// after the barrier the raw B of stage t + 2 and the A of stage t + 1 are loaded, and stage t
-// is multiplied while the raw B of stage t + 1 (loaded during stage t - 1) is requantised into
-// the other buffer between the matrix groups.  One barrier per stage, as in mainloop.
-template <int F>
-MOE_DEV void mainloop_tb(uint8_t* lds, const TileLoads<F>& L, TransB& tb, int nk, v16f (&acc)[F][2]) {
-  static_for<F>([&]<int mi>() {
-    acc[mi][0] = (v16f){};
-    acc[mi][1] = (v16f){};
-  });
-  if (nk <= 0) return;
-  tb.load_next(0);
-  issue_a_stage<F, 2, 0>(L, lds, 0);
-  tb.advance();
-  tb.requant_pairs<0, 8>(lds);
-  if (nk > 1) {
-    tb.load_next(1);
-    tb.advance();
-  }
-  for (int t = 0; t < nk; ++t) {
-    // A of stage t has landed; every wave wrote its share of stage t's B and is done with t - 1
-    wait_loads_and_sync<0>();
-    if (t + 2 < nk) tb.load_next(t + 2);
-    if (t + 1 < nk) issue_a_stage<F, 2, 0>(L, lds, t + 1);
-    // (in the last stage this requantises stale registers into the B region of the free buffer,
-    // which nothing reads afterwards: cheaper than a branch)
-    compute_stage<F>(lds + (t % 2) * STAGE_BYTES, acc, RequantHook{tb, lds + ((t + 1) % 2) * STAGE_BYTES});
-    // unconditional (past the last load it copies stale registers that nothing uses): a branch
-    // after the matrix instructions would let the compiler sink them below the vector work
-    tb.advance();
   }
 }
 
@@ -542,9 +384,24 @@ MOE_DEV void compute_stage8(const uint8_t* st, v16f (&acc)[(F + 1) / 2][2]) {
   });
 }
 
-// acc = this wave's part of A_tile * B_tile^T over K = 128 nk; one barrier per stage.
-template <int F>
-MOE_DEV void mainloop8(uint8_t* lds, const TileLoads8<F>& L, int nk, v16f (&acc)[(F + 1) / 2][2]) {
+struct NoAfterStage {
+  MOE_DEV void operator()(const uint8_t*, int) const {}
+};
+
+// An empty statement that reads and rewrites the accumulators in place: code after it cannot
+// start before the matrix instructions that produce them have been issued.
+MOE_DEV void pin_vgprs(v16f& a, v16f& b) { asm volatile("" : "+v"(a), "+v"(b)::"memory"); }
+template <int FH>
+MOE_DEV void pin_acc(v16f (&acc)[FH][2]) {
+  static_for<FH>([&]<int m>() { pin_vgprs(acc[m][0], acc[m][1]); });
+}
+
+// acc = this wave's part of A_tile * B_tile^T over K = 128 nk; one barrier per stage.  After the
+// matrix instructions of stage t the workgroup calls after_stage(staged buffer, t): vector work
+// on the stage that is still resident (the next barrier retires the buffer).
+template <int F, class AfterStage>
+MOE_DEV void mainloop8(uint8_t* lds, const TileLoads8<F>& L, int nk, v16f (&acc)[(F + 1) / 2][2],
+                       const AfterStage& after_stage) {
   static_for<(F + 1) / 2>([&]<int m>() {
     acc[m][0] = (v16f){};
     acc[m][1] = (v16f){};
@@ -555,7 +412,96 @@ MOE_DEV void mainloop8(uint8_t* lds, const TileLoads8<F>& L, int nk, v16f (&acc)
     wait_loads_and_sync<0>();  // stage t has landed; every wave is done with stage t - 1
     if (t + 1 < nk) issue_stage8<F>(L, lds, t + 1);
     compute_stage8<F>(lds + (t % 2) * STAGE_BYTES, acc);
+    if constexpr (!std::is_same_v<AfterStage, NoAfterStage>) {
+      // an empty statement that rewrites the accumulators: the stage's matrix instructions
+      // issue before the vector work below (a branch there would otherwise let the compiler
+      // sink them past it, keeping every A/B fragment live across the vector work)
+      pin_acc<(F + 1) / 2>(acc);
+      after_stage((const uint8_t*)(lds + (t % 2) * STAGE_BYTES), t);
+    }
   }
+}
+
+template <int F>
+MOE_DEV void mainloop8(uint8_t* lds, const TileLoads8<F>& L, int nk, v16f (&acc)[(F + 1) / 2][2]) {
+  mainloop8<F>(lds, L, nk, acc, NoAfterStage{});
+}
+
+// ---------------------------------------------------------------------------------------------
+// Transposed requantisation of a staged weight slice (512 threads).
+//
+// The backward pass contracts the expert weights over the other axis (dgrad of the down GEMM
+// over d, of the gate/up GEMM over 2I), so it needs W^T quantised along that axis: every 32
+// consecutive weight rows of one column are dequantised exactly (e4m3 code x 2^(e - 127) is a
+// float32) and quantised again with their own e8m0 exponent.  The forward GEMMs stream every
+// weight slice through LDS anyway; a stage's B part holds 256 weight rows x 128 K values, i.e.
+// whole 32-row blocks of 128 columns, so the transposed codes are produced there and written
+// to HBM once (no separate pass that reads the weights again).
+//
+// Wave w takes staged rows [32w, 32w + 32) (one block along the requantisation axis): lane l
+// reads rows 32w + 4(l >> 3) .. + 4 at 16-byte chunk l & 7 (columns 16(l & 7) .. + 16) and the
+// four rows' scale bytes; the block maximum of a column spans the 8 lanes l ^ 8, l ^ 16, l ^ 32
+// (a row rotation, then the two lane-swap instructions).  A lane then writes its 4 codes of
+// each column as one 4-byte word of the transposed row and 2 of the 16 columns' scale bytes.
+//   wt  [K][ldt] codes, wts [K][ldt / 32] scales: transposed weight of the expert;
+//   k0: first K index (column of the weight) of the stage; orow: first transposed-row index
+//   of staged row block w, or -1 to skip the block.
+MOE_DEV void requant_stage_t8(const uint8_t* st, int k0, int orow, uint8_t* wt, uint8_t* wts, int ldt) {
+  const int w = threadIdx.x >> 6, l = lane_id();
+  const int g = l & 7, rq = l >> 3;
+  if (orow < 0) return;  // wave-uniform
+  // opaque per call: keeps the compiler from hoisting the 16 columns' addresses out of the GEMM's
+  // K loop, where they would stay live (and spill) across the matrix work
+  asm volatile("" : "+s"(ldt), "+s"(wt), "+s"(wts));
+  const int r0 = 32 * w + 4 * rq;
+  v4i raw[4];
+  float f[4];
+  __builtin_amdgcn_sched_barrier(0);  // after the stage's matrix instructions
+  static_for<4>([&]<int j>() {
+    const int r = r0 + j;
+    raw[j] = *(const v4i*)(st + A_STAGE + r * KS + 16 * (g ^ swz(r)));
+    f[j] = e8m0_scale(st[DATA_BYTES + TM * 4 + 4 * r + (g >> 1)]);
+  });
+  const size_t col0 = (size_t)(k0 + 16 * g);
+  uint8_t* out = wt + col0 * ldt + orow + 4 * rq;
+  // four quarters of 4 columns: word P of every row piece holds columns 4P .. 4P + 3 (few
+  // registers live at a time: this runs inside the GEMM's main loop)
+  uint32_t sbytes[4];  // the 16 columns' scale bytes, byte c % 4 of word c / 4 (same in the 8 lanes)
+  static_for<4>([&]<int P>() {
+    float v[4][4];
+    static_for<4>([&]<int j>() {
+      const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(raw[j][P], false);
+      const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(raw[j][P], true);
+      v[j][0] = lo[0] * f[j];
+      v[j][1] = lo[1] * f[j];
+      v[j][2] = hi[0] * f[j];
+      v[j][3] = hi[1] * f[j];
+    });
+    sbytes[P] = 0;
+    static_for<4>([&]<int c>() {
+      const float m = fmaxf(fmaxf(fabsf(v[0][c]), fabsf(v[1][c])), fmaxf(fabsf(v[2][c]), fabsf(v[3][c])));
+      // non-negative floats order like their bit patterns: the lane maxima cross as integers
+      uint32_t u = __float_as_uint(m);
+      u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x128, 0xF, 0xF, false));  // l ^ 8
+      const auto p16 = __builtin_amdgcn_permlane16_swap((int)u, (int)u, false, false);        // l ^ 16
+      u = max((uint32_t)p16[0], (uint32_t)p16[1]);
+      const auto p32 = __builtin_amdgcn_permlane32_swap((int)u, (int)u, false, false);        // l ^ 32
+      u = max((uint32_t)p32[0], (uint32_t)p32[1]);
+      const uint32_t byte = e8m0_from_amax(__uint_as_float(u));
+      const float inv = e8m0_inv_scale(byte);
+      const uint32_t codes = pack4_e4m3(v[0][c] * inv, v[1][c] * inv, v[2][c] * inv, v[3][c] * inv);
+      *(uint32_t*)(out + (size_t)(4 * P + c) * ldt) = codes;
+      sbytes[P] |= byte << (8 * c);
+    });
+    __builtin_amdgcn_sched_barrier(0);  // one quarter's values live at a time
+  });
+  // lane (g, rq) stores the scale bytes of columns rq and rq + 8 (no branch)
+  const uint32_t sh = 8 * (rq & 3);
+  const uint32_t lo = (rq & 4) ? sbytes[1] : sbytes[0];
+  const uint32_t hi = (rq & 4) ? sbytes[3] : sbytes[2];
+  uint8_t* sp = wts + (col0 + rq) * (ldt / 32) + orow / 32;
+  sp[0] = (uint8_t)(lo >> sh);
+  sp[(size_t)8 * (ldt / 32)] = (uint8_t)(hi >> sh);
 }
 
 // Quantise 32 consecutive columns of one row held by the 32 lanes of a half-wave:

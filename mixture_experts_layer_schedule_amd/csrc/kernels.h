@@ -23,6 +23,7 @@ struct GateUpArgs {
   const uint8_t *xq, *xs, *w1q, *w1s;
   float *g, *u;
   uint8_t *hq, *hs;
+  uint8_t *w1t, *w1ts;  // [NX][d][2I] + [NX][d][2I/32]: W1 transposed, requantised along 2I (NULL: skip)
   int d, I;
 };
 
@@ -30,13 +31,14 @@ struct DownArgs {
   SchedView s;
   const uint8_t *hq, *hs, *w2q, *w2s;
   float* yslot;
+  uint8_t *w2t, *w2ts;  // [NX][I][d] + [NX][I][d/32]: W2 transposed, requantised along d (NULL: skip)
   int d, I;
 };
 
 struct DgradDownArgs {
   SchedView s;
   const uint8_t *dyq, *dys;
-  const uint8_t *w2q, *w2s;  // forward weight [E+S][d][I] + [E+S][d][I/32], requantised along d in the kernel
+  const uint8_t *w2t, *w2ts;  // [NX][I][d] + [NX][I][d/32] (written by the forward down GEMM)
   const float *w, *g, *u;
   uint8_t *dguq, *dgus;
   int d, I;
@@ -45,7 +47,7 @@ struct DgradDownArgs {
 struct DgradGateUpArgs {
   SchedView s;
   const uint8_t *dguq, *dgus;
-  const uint8_t *w1q, *w1s;  // forward weight [E+S][2I][d] + [E+S][2I][d/32], requantised along 2I in the kernel
+  const uint8_t *w1t, *w1ts;  // [NX][d][2I] + [NX][d][2I/32] (written by the forward gate/up GEMM)
   float* dxslot;
   int d, I;
 };
@@ -113,8 +115,9 @@ hipError_t launch_token_requant(const TokArgs&, int tiles_bound, hipStream_t);
 // Router, top-k and schedule.
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_r, const float* bias, float* logits,
                                 int T, int d, int E, hipStream_t);
+// status: device status word (MOE_DEV_NONFINITE_LOGIT when a logit is NaN or infinite)
 hipError_t launch_topk(const float* logits, int T, int E, int k, int score, int32_t* idx, float* w,
-                       hipStream_t);
+                       int32_t* status, hipStream_t);
 struct SchedBuild {
   const int32_t* idx;   // [T, k]
   int32_t* blkcnt;      // [nblk, E] scratch

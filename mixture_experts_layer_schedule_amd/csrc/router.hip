@@ -71,22 +71,29 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
 //
 // One wave per token.  Experts are ranked by logit, best first; equal logits go to the lower
 // expert index.  Weights: softmax over the k selected logits, or sigmoid scores normalised by
-// their sum.
+// their sum.  A NaN logit ranks as -inf, so every token still selects k distinct valid experts
+// (the ranking is total); a non-finite logit also sets MOE_DEV_NONFINITE_LOGIT in the status word.
 
 constexpr int kMaxPerLane = 8;  // E <= 512
+constexpr int32_t kDevNonfiniteLogit = 2;  // MOE_DEV_NONFINITE_LOGIT
 
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ L, int T, int E, int k, int score,
-                                              int32_t* __restrict__ idx, float* __restrict__ w) {
+                                              int32_t* __restrict__ idx, float* __restrict__ w,
+                                              int32_t* __restrict__ status) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int l = lane_id();
   float v[kMaxPerLane];
   const int nper = (E + 63) / 64;
+  bool nonfinite = false;
 #pragma unroll
   for (int q = 0; q < kMaxPerLane; ++q) {
     int e = l + 64 * q;
-    v[q] = (q < nper && e < E) ? L[(size_t)t * E + e] : -INFINITY;
+    float x = (q < nper && e < E) ? L[(size_t)t * E + e] : -INFINITY;
+    if (q < nper && e < E && !isfinite(x)) nonfinite = true;
+    v[q] = x == x ? x : -INFINITY;  // NaN ranks as -inf
   }
+  if (__any(nonfinite) && l == 0) __hip_atomic_store(status, kDevNonfiniteLogit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   uint32_t taken = 0;
   float sel_v[16];
   int sel_e[16];
@@ -218,8 +225,8 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_r, const fl
 }
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int score, int32_t* idx, float* w,
-                       hipStream_t st) {
-  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, k, score, idx, w);
+                       int32_t* status, hipStream_t st) {
+  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, k, score, idx, w, status);
   return hipGetLastError();
 }
 

@@ -22,7 +22,7 @@ class MoeLayer:
         self.device = torch.device(device)
         score_fn = MOE_SCORE_SOFTMAX if score == "softmax" else MOE_SCORE_SIGMOID
         self.cfg = make_config(T, d, E, k, inter, n_shared, score_fn, ring_rows, chunk_rows, producer_wgs, flags)
-        ws, self.layout = moe_query(self.cfg)
+        ws, self.layout, self.wlayout = moe_query(self.cfg, with_workspace_layout=True)
         dev = self.device
         self.saved = torch.empty(self.layout.total, dtype=torch.uint8, device=dev)
         self.workspace = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
@@ -45,8 +45,7 @@ class MoeLayer:
     def from_config(cls, cfg, **kw):
         """From a moe_inputs.LayerConfig."""
         return cls(cfg.T, cfg.d, cfg.E, cfg.k, cfg.inter, cfg.score, cfg.n_shared,
-                   ring_rows=kw.pop("ring_rows", cfg.ring_rows), with_backward=kw.pop("with_backward", cfg.backward),
-                   **kw)
+                   with_backward=kw.pop("with_backward", cfg.backward), **kw)
 
     # ------------------------------------------------------------------ inputs
 
@@ -82,8 +81,8 @@ class MoeLayer:
         return self.y
 
     def backward(self, stream=None, f32=True):
-        moe_bwd(self.cfg, self.dy, self.x, self.w_r, self.w1q, self.w1s, self.w2q, self.w2s, self.saved, self.dx,
-                self.dx32 if f32 else None, self.dw_r, self.dw1, self.dw2, self.workspace, stream)
+        moe_bwd(self.cfg, self.dy, self.x, self.w_r, self.saved, self.dx, self.dx32 if f32 else None, self.dw_r,
+                self.dw1, self.dw2, self.workspace, stream)
         return self.dx
 
     # ------------------------------------------------------------------ saved state
@@ -102,8 +101,31 @@ class MoeLayer:
             "g": (torch.float32, (RS, I)), "u": (torch.float32, (RS, I)),
             "hq": (torch.uint8, (RS, I)), "hs": (torch.uint8, (RS, I // 32)),
             "yslot": (torch.float32, (T, k + S, d)),
+            "w1t": (torch.uint8, (NX, d, 2 * I)), "w1ts": (torch.uint8, (NX, d, 2 * I // 32)),
+            "w2t": (torch.uint8, (NX, I, d)), "w2ts": (torch.uint8, (NX, I, d // 32)),
         }
         dt, shape = spec[name]
         off = getattr(self.layout, name)
         n = int(np.prod(shape)) * torch.tensor([], dtype=dt).element_size()
         return self.saved[off:off + n].view(dt).view(shape)
+
+    def workspace_tensor(self, name: str) -> torch.Tensor:
+        """A typed view of one field of the workspace (see moe_workspace_layout)."""
+        T, d, k, I, S = self.T, self.d, self.k, self.I, self.S
+        RS = T * k + S * T
+        ld = int(self.wlayout.tok_stride)
+        spec = {
+            "status": (torch.int32, (1,)),
+            "dyq": (torch.uint8, (T, d)), "dys": (torch.uint8, (T, d // 32)),
+            "dw": (torch.float32, (T, k)), "dl": (torch.float32, (T, k)),
+            "dguq": (torch.uint8, (RS, 2 * I)), "dgus": (torch.uint8, (RS, 2 * I // 32)),
+            "dxslot": (torch.float32, (T, k + S, d)),
+            "xt": (torch.uint8, (d, ld)), "xts": (torch.uint8, (d, ld // 32)),
+            "ht": (torch.uint8, (I, ld)), "hts": (torch.uint8, (I, ld // 32)),
+            "dyt": (torch.uint8, (d, ld)), "dyts": (torch.uint8, (d, ld // 32)),
+            "dgut": (torch.uint8, (2 * I, ld)), "dguts": (torch.uint8, (2 * I, ld // 32)),
+        }
+        dt, shape = spec[name]
+        off = getattr(self.wlayout, name)
+        n = int(np.prod(shape)) * torch.tensor([], dtype=dt).element_size()
+        return self.workspace[off:off + n].view(dt).view(shape)

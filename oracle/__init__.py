@@ -45,5 +45,8 @@ from .layer import (  # noqa: F401
     router_logits,
     routing_weights,
     select_topk,
+    swiglu,
+    swiglu_backward,
+    token_quantize,
     token_requant,
 )

@@ -29,7 +29,7 @@ import numpy as np
 from .layer import BLOCK, _qdq, _sigmoid
 from .mxfp8 import quantize_range
 
-EPS_ACC = 2.0 ** -14
+EPS_ACC = 2.0 ** -15  # the GPU tests' model: measured G / U errors reach 2^-15.96 * sum|a b| (K = 256)
 F32_SLACK = 2.0 ** -18   # relative error of float32 elementwise epilogues (exp, products)
 
 

@@ -51,23 +51,45 @@ def _qdq(a: np.ndarray, axis: int, quant: bool):
     return q, s, dequantize(q, s, axis=axis)
 
 
-def token_requant(a: np.ndarray, quant: bool = True) -> np.ndarray:
-    """Requantise rows of one expert along the token axis (axis 0) and dequantise.
+def token_quantize(a: np.ndarray):
+    """MXFP8 codes and scales of one expert's rows quantised along the token axis (axis 0).
 
     Reading of "requantisation of transposed operands" for the weight-gradient
     GEMMs, whose reduction axis is the token axis: blocks of 32 consecutive rows
     start at the first row of the expert's segment, and a ragged tail is padded
-    with zero rows (zeros change neither a block maximum nor a sum).
+    with zero rows (zeros change neither a block maximum nor a sum).  Returns
+    (codes [npad, ...], scales [npad / 32, ...]) with npad = n rounded up to 32.
     """
     a = np.asarray(a, dtype=np.float64)
-    if not quant:
-        return a
     n = a.shape[0]
     npad = -(-n // BLOCK) * BLOCK
     padded = np.zeros((npad,) + a.shape[1:], dtype=np.float64)
     padded[:n] = a
-    q, s = quantize(padded, axis=0)
-    return dequantize(q, s, axis=0)[:n]
+    return quantize(padded, axis=0)
+
+
+def token_requant(a: np.ndarray, quant: bool = True) -> np.ndarray:
+    """One expert's rows requantised along the token axis (``token_quantize``), dequantised."""
+    a = np.asarray(a, dtype=np.float64)
+    if not quant:
+        return a
+    q, s = token_quantize(a)
+    return dequantize(q, s, axis=0)[: a.shape[0]]
+
+
+def swiglu(G: np.ndarray, U: np.ndarray) -> np.ndarray:
+    """h = silu(G) U = G sigmoid(G) U (the expert's gated activation)."""
+    G = np.asarray(G, dtype=np.float64)
+    return G * _sigmoid(G) * np.asarray(U, dtype=np.float64)
+
+
+def swiglu_backward(dH: np.ndarray, G: np.ndarray, U: np.ndarray):
+    """(dG, dU) of h = silu(G) U for upstream dH: with s = sigmoid(G),
+    dG = dH U s (1 + G (1 - s)) and dU = dH G s."""
+    G = np.asarray(G, dtype=np.float64)
+    U = np.asarray(U, dtype=np.float64)
+    s = _sigmoid(G)
+    return dH * U * s * (1.0 + G * (1.0 - s)), dH * G * s
 
 
 # ----------------------------------------------------------------------------
@@ -176,7 +198,7 @@ def expert_forward(A: np.ndarray, W1: np.ndarray, W2: np.ndarray, quant: bool = 
     I = W1.shape[0] // 2
     G = A @ W1[:I].T
     U = A @ W1[I:].T
-    h = G * _sigmoid(G) * U
+    h = swiglu(G, U)
     if quant:
         h = _f32(h)
     Hq, Hs, H = _qdq(h, 1, quant)
@@ -215,9 +237,7 @@ def expert_backward(fw: ExpertForward, A: np.ndarray, DYrows: np.ndarray, wrow: 
       precision for that decision).
     """
     dH = wrow[:, None] * (DYrows @ W2t)
-    s = _sigmoid(fw.G)
-    dG = dH * fw.U * s * (1.0 + fw.G * (1.0 - s))
-    dU = dH * fw.G * s
+    dG, dU = swiglu_backward(dH, fw.G, fw.U)
     dGU = np.concatenate([dG, dU], axis=1)
     if quant:
         dGU = _f32(dGU)

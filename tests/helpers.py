@@ -10,6 +10,26 @@ import moe_inputs
 import oracle
 
 
+# Small layers checked whole: the tiny workload, two mid-size layers (one with a shared expert and
+# a Zipf router bias) and edge cases:
+MID = moe_inputs.LayerConfig("mid", T=512, d=512, E=16, k=4, inter=256, score="softmax", seed=7)
+MID_SIG = moe_inputs.LayerConfig("mid_sig_shared", T=384, d=256, E=24, k=6, inter=384, score="sigmoid", seed=8,
+                                 n_shared=1, zipf_s=1.1, zipf_lam=0.5)
+# a ragged token count (not a multiple of any tile or block) with 12 experts; a
+# strongly skewed router that leaves 8 of 16 experts without rows and one with a single row;
+# k = E (every expert sees every token, T ragged); k = 1 with a shared expert and d = 384 (an odd
+# number of K stages); the routing limits.
+RAGGED = moe_inputs.LayerConfig("ragged", T=200, d=256, E=12, k=3, inter=128, score="softmax", seed=9)
+EMPTY = moe_inputs.LayerConfig("empty_experts", T=72, d=128, E=16, k=2, inter=128, score="sigmoid", seed=10,
+                               zipf_s=1.1, zipf_lam=2.0)
+K_EQ_E = moe_inputs.LayerConfig("k_eq_e", T=65, d=128, E=4, k=4, inter=256, score="softmax", seed=11)
+K1_SHARED = moe_inputs.LayerConfig("k1_shared", T=130, d=384, E=6, k=1, inter=128, score="sigmoid", seed=12,
+                                   n_shared=1)
+# the API's routing limits: 512 experts, top-16 (most experts see a few rows, many none)
+MAX_ROUTE = moe_inputs.LayerConfig("max_route", T=70, d=128, E=512, k=16, inter=128, score="softmax", seed=13)
+CASES = [moe_inputs.CONFIGS["tiny"], MID, MID_SIG, RAGGED, EMPTY, K_EQ_E, K1_SHARED, MAX_ROUTE]
+
+
 def log(*a):
     print(*a, flush=True)
     sys.stdout.flush()

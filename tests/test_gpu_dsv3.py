@@ -5,10 +5,14 @@ backward).  The oracle cannot run the whole layer in a test's time, so it checks
 compute piece by piece on the same seeded inputs:
 
 * routing of every token (top-k on float32 logits) and the whole schedule, bit-exact;
-* x quantisation, bit-exact;
-* two experts (median and maximum load) end to end: G/U within the accumulation model, H codes
-  unique-or-admissible, their Y rows, dW1 and dW2 within 1e-2 RMS + envelope;
-* a sampled token end to end (all its experts): y and dx within 1e-2 RMS + envelope.
+* x and dy quantisation, bit-exact;
+* six experts (least, median and most loaded, three seeded others) through every stage on the
+  GPU's own intermediates (stages.py): quantised weights, W1t / W2t and the token-axis operands
+  bit-exact, H and [dG dU] codes exact outside the float32 slack of a rounding boundary, G, U, Y
+  slots, dX slots, dW1 and dW2 within 1e-2 RMS;
+* dw, dL of every token and the whole dW_router within 1e-2 RMS;
+* a sampled token through the combine and the dx reduction within 1e-2 RMS, and against the
+  oracle's own end-to-end result within 1e-2 RMS + the envelope of code flips.
 """
 import numpy as np
 import pytest
@@ -17,6 +21,7 @@ import moe_inputs
 import oracle
 from oracle import envelope
 from oracle.layer import _qdq
+import stages
 from helpers import log, rms, to_np
 
 pytestmark = pytest.mark.gpu
@@ -101,63 +106,84 @@ def _check(name, got, ref, bound):
     assert np.all(err <= TOL * r + bound), name
 
 
-def test_sampled_experts_end_to_end(run):
+@pytest.fixture(scope="module")
+def view(run):
     cfg, inp, layer, experts = run
-    counts = to_np(layer.saved_tensor("counts"))
-    offs = to_np(layer.saved_tensor("offsets"))
-    perm = to_np(layer.saved_tensor("perm"))
-    wflat = oracle.routing_weights(oracle.router_logits(inp.x, inp.w_r), to_np(layer.saved_tensor("idx")),
-                                   cfg.score).reshape(-1)
-    order = np.argsort(counts)
-    picks = [int(order[len(order) // 2]), int(order[-1])]
-    xq, xs = oracle.quantize(inp.x.astype(np.float64), axis=1)
-    X = oracle.dequantize(xq, xs, axis=1)
-    dyq, dys = oracle.quantize(inp.dy.astype(np.float64), axis=1)
-    DY = oracle.dequantize(dyq, dys, axis=1)
-    G = layer.saved_tensor("g")
-    U = layer.saved_tensor("u")
-    for e in picks:
-        lo, hi = int(offs[e]), int(offs[e + 1])
-        toks = perm[lo:hi] // cfg.k
-        wrow = wflat[perm[lo:hi]]
-        W1, W2 = experts(e)
-        log(f"dsv3: expert {e} with {hi - lo} rows")
-        fe = oracle.expert_forward(X[toks], W1, W2)
-        eG, eU, Hlo, Hhi, devH, BY = envelope.expert_forward_envelope(fe, X[toks], W1, W2, EPS)
-        g = to_np(G[lo:hi]).astype(np.float64)
-        u = to_np(U[lo:hi]).astype(np.float64)
-        log(f"  G err / model max {np.max(np.abs(g - fe.G) / eG):.3f}")
-        assert np.all(np.abs(g - fe.G) <= eG) and np.all(np.abs(u - fe.U) <= eU)
-        H = oracle.dequantize(to_np(layer.saved_tensor("hq")[lo:hi]), to_np(layer.saved_tensor("hs")[lo:hi]), axis=1)
-        uniq = Hlo == Hhi
-        assert np.all(H[uniq] == fe.H[uniq]) and np.all((H >= Hlo) & (H <= Hhi))
-        ys = layer.saved_tensor("yslot").view(-1, cfg.d)
-        slots = (perm[lo:hi] // cfg.k) * cfg.k + perm[lo:hi] % cfg.k
-        _check(f"Y rows of expert {e}", to_np(ys[slots]), fe.Y, BY)
-        W2t = _qdq(W2, 0, True)[2]
-        W1t = _qdq(W1, 0, True)[2]
-        be = oracle.expert_backward(fe, X[toks], DY[toks], wrow, W1t, W2t)
-        _, _, _, bdw1, bdw2 = envelope.expert_backward_envelope(fe, be, X[toks], DY[toks], wrow, W1, W2, eG, eU,
-                                                                devH, EPS)
-        _check(f"dW1[{e}]", to_np(layer.dw1[e]), be.dW1, bdw1)
-        _check(f"dW2[{e}]", to_np(layer.dw2[e]), be.dW2, bdw2)
+    return stages.LayerView(cfg, inp, layer)
+
+
+def _picks(v, n_random=3):
+    """Least-loaded, median-load and most-loaded expert, and a few others (seeded)."""
+    counts = v.counts[:v.cfg.E]
+    order = np.argsort(counts, kind="stable")
+    rng = np.random.default_rng(4)
+    picks = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
+    picks += [int(e) for e in rng.choice(np.setdiff1d(np.arange(v.cfg.E), picks), n_random, replace=False)]
+    return picks
+
+
+def test_sampled_experts_every_stage(run, view):
+    """Every stage of six experts on the GPU's own intermediates (stages.py): W1t / W2t, the
+    token-axis operands bit-exact; H and [dG dU] codes exact outside the float32 slack; G, U,
+    Y slots, dX slots, dW1, dW2 within 1e-2 RMS."""
+    cfg, inp, layer, experts = run
+    st = stages.StageStats()
+    for e in _picks(view):
+        log(f"dsv3: expert {e} ({int(view.counts[e])} rows): forward stages")
+        w1, w2 = moe_inputs.expert_weights(cfg, e)
+        W1, W2, _ = stages.check_expert_forward(view, e, w1, w2, st)
+        log(f"dsv3: expert {e}: backward stages")
+        stages.check_expert_backward(view, e, W1, W2, st)
+    st.report("dsv3")
+
+
+def test_router_backward_every_token(run, view):
+    """dw, dL on every token and the whole dW_router, from the GPU's Y slots, logits and weights."""
+    cfg, inp, layer, experts = run
+    st = stages.StageStats()
+    dL = stages.check_router_backward(view, st)
+    dLfull = np.zeros((cfg.T, cfg.E))
+    np.put_along_axis(dLfull, view.idx.astype(np.int64), dL, axis=1)
+    st.err("dW_router", to_np(layer.dw_r), dLfull.T @ inp.x.astype(np.float64))
+    st.report("dsv3")
 
 
 @pytest.mark.parametrize("t", [4321])
-def test_sampled_token_end_to_end(run, t):
+def test_sampled_token_end_to_end(run, view, t):
+    """One token through every stage (its k experts): the combine of its Y slots into y, and dx
+    from its dX slot rows (oracle dgrad of the GPU's [dG dU]) plus the router term, both within
+    1e-2 RMS; then the token against the oracle's own end-to-end result within 1e-2 RMS plus the
+    admissible envelope of the code flips (a secondary check)."""
     cfg, inp, layer, experts = run
+    st = stages.StageStats()
+    ys = to_np(layer.saved_tensor("yslot")[t]).astype(np.float64)
+    st.err(f"y[{t}]", to_np(layer.y32[t]), view.w[t] @ ys[:cfg.k])
+    # dX slot rows of the token from the GPU's [dG dU] rows
+    rows = view.pos[t]
+    dguq = to_np(layer.workspace_tensor("dguq")[rows])
+    dgus = to_np(layer.workspace_tensor("dgus")[rows])
+    DGU = oracle.dequantize(dguq, dgus, axis=1)
+    dX = np.zeros((cfg.k, cfg.d))
+    for j, e in enumerate(view.idx[t]):
+        W1t = _qdq(experts(int(e))[0], 0, True)[2]
+        dX[j] = DGU[j] @ W1t
+    st.err(f"dX slots[{t}]", to_np(layer.workspace_tensor("dxslot")[t]), dX)
+    dL = stages.check_router_backward(view, st, tokens=[t])[0]
+    wr = inp.w_r.astype(np.float64)
+    dx = dX.sum(axis=0) + dL @ wr[view.idx[t]]
+    st.err(f"dx[{t}]", to_np(layer.dx32[t]), dx)
+    st.report("dsv3")
+    # secondary: the oracle's own end-to-end result, within 1e-2 RMS + the envelope of code flips
     x = inp.x[t:t + 1].astype(np.float64)
     dy = inp.dy[t:t + 1].astype(np.float64)
-    log(f"dsv3: token {t}: oracle forward")
+    log(f"dsv3: token {t}: oracle forward / backward / envelopes")
     fw = oracle.layer_forward(x, inp.w_r, experts, cfg.k, cfg.score)
-    log(f"dsv3: token {t}, experts {list(fw.idx[0])}: oracle backward")
     bw = oracle.layer_backward(fw, dy, x, inp.w_r, experts, cfg.score, expert_subset=sorted(fw.experts))
-    log(f"dsv3: token {t}: envelopes")
     fenv = envelope.forward_envelope(fw, experts, EPS)
     benv = envelope.backward_envelope(fw, bw, fenv, dy, x, inp.w_r, experts, cfg.score)
     assert np.array_equal(to_np(layer.saved_tensor("idx")[t]), fw.idx[0])
-    _check(f"y[{t}]", to_np(layer.y32[t:t + 1]), fw.y, fenv.By)
-    _check(f"dx[{t}]", to_np(layer.dx32[t:t + 1]), bw.dx, benv.Bdx)
+    _check(f"y[{t}] end to end", to_np(layer.y32[t:t + 1]), fw.y, fenv.By)
+    _check(f"dx[{t}] end to end", to_np(layer.dx32[t:t + 1]), bw.dx, benv.Bdx)
 
 
 def test_bitwise_run_to_run(run):

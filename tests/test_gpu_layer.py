@@ -21,22 +21,7 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-2
 EPS = 2.0 ** -15  # accumulation model of the matrix-core GEMMs (checked on G and U)
 
-MID = moe_inputs.LayerConfig("mid", T=512, d=512, E=16, k=4, inter=256, score="softmax", seed=7)
-MID_SIG = moe_inputs.LayerConfig("mid_sig_shared", T=384, d=256, E=24, k=6, inter=384, score="sigmoid", seed=8,
-                                 n_shared=1, zipf_s=1.1, zipf_lam=0.5)
-# Edge cases: a ragged token count (not a multiple of any tile or block) with 12 experts; a
-# strongly skewed router that leaves 8 of 16 experts without rows and one with a single row;
-# k = E (every expert sees every token, T ragged); k = 1 with a shared expert and d = 384 (an odd
-# number of K stages); the routing limits.
-RAGGED = moe_inputs.LayerConfig("ragged", T=200, d=256, E=12, k=3, inter=128, score="softmax", seed=9)
-EMPTY = moe_inputs.LayerConfig("empty_experts", T=72, d=128, E=16, k=2, inter=128, score="sigmoid", seed=10,
-                               zipf_s=1.1, zipf_lam=2.0)
-K_EQ_E = moe_inputs.LayerConfig("k_eq_e", T=65, d=128, E=4, k=4, inter=256, score="softmax", seed=11)
-K1_SHARED = moe_inputs.LayerConfig("k1_shared", T=130, d=384, E=6, k=1, inter=128, score="sigmoid", seed=12,
-                                   n_shared=1)
-# the API's routing limits: 512 experts, top-16 (most experts see a few rows, many none)
-MAX_ROUTE = moe_inputs.LayerConfig("max_route", T=70, d=128, E=512, k=16, inter=128, score="softmax", seed=13)
-CASES = [moe_inputs.CONFIGS["tiny"], MID, MID_SIG, RAGGED, EMPTY, K_EQ_E, K1_SHARED, MAX_ROUTE]
+from helpers import CASES, MID_SIG as MID_SIG_CFG  # noqa: E402
 
 
 def _bf16_rne(a32):
@@ -231,3 +216,68 @@ def test_serial_and_concurrent_backward_identical(pair):
         layer.cfg.flags &= ~moe.MOE_F_SERIAL_BWD
     for name, a, b in zip(("dx", "dW1", "dW2", "dW_r"), ref, (layer.dx32, layer.dw1, layer.dw2, layer.dw_r)):
         assert torch.equal(a, b), name
+
+
+def test_nonfinite_logits_route_to_valid_experts():
+    """A token whose router logits are all NaN (a NaN in its x row) still selects k distinct valid
+    experts (NaN ranks as -inf, ties to the lower index: experts 0..k-1), the schedule stays a
+    bijection, and the device status word reports MOE_DEV_NONFINITE_LOGIT."""
+    import torch
+    import mixture_experts_layer_schedule_amd as moe
+    cfg = moe_inputs.CONFIGS["tiny"]
+    inp = moe_inputs.layer_inputs(cfg)
+    x = inp.x_bits.copy()
+    x[5, 7] = 0x7FC0   # a bf16 NaN: every logit of token 5 is NaN
+    x[9, 3] = 0x7F80   # +inf: token 9's logits are +-inf or NaN
+    layer = gpu_layer(cfg, False, inp=moe_inputs.LayerInputs(cfg, x, inp.w_r_bits, inp.bias, None),
+                      flags=moe.MOE_F_FORWARD_ONLY)
+    idx = to_np(layer.saved_tensor("idx"))
+    assert idx.min() >= 0 and idx.max() < cfg.E
+    assert all(len(set(r)) == cfg.k for r in idx)
+    assert list(idx[5]) == list(range(cfg.k))
+    perm = to_np(layer.saved_tensor("perm"))
+    assert np.array_equal(np.sort(perm), np.arange(cfg.T * cfg.k))
+    counts = to_np(layer.saved_tensor("counts"))
+    assert counts.sum() == cfg.T * cfg.k
+    # every other token routes exactly as the oracle does
+    L = oracle.router_logits(moe_inputs.bf16_values(x).astype(np.float64), inp.w_r)
+    ok = np.isfinite(L).all(axis=1)
+    assert ok.sum() == cfg.T - 2
+    assert np.array_equal(idx[ok], oracle.select_topk(L[ok], cfg.k))
+    assert moe.moe_device_status(layer.workspace) == moe.MOE_DEV_NONFINITE_LOGIT
+    torch.cuda.synchronize()
+
+
+def test_forward_and_backward_do_not_block_the_host():
+    """moe_fwd / moe_bwd only enqueue: behind a long-running kernel on the same stream both calls
+    return while the stream is still busy (no host synchronisation inside the layer)."""
+    import time
+    import torch
+    cfg = moe_inputs.CONFIGS["tiny"].with_(backward=True)
+    layer = gpu_layer(cfg, True)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(200_000_000)   # a bounded spin kernel: tens of milliseconds or more
+    t0 = time.perf_counter()
+    layer.forward()
+    layer.backward()
+    t_call = time.perf_counter() - t0
+    busy = not stream.query()
+    stream.synchronize()
+    t_all = time.perf_counter() - t0
+    log(f"host time of forward + backward calls {t_call * 1e3:.2f} ms; until the stream drained {t_all * 1e3:.1f} ms")
+    assert busy, "the stream finished before the calls returned"
+    assert t_call < 0.5 * t_all
+
+
+def test_forward_only_matches_default_forward():
+    """MOE_F_FORWARD_ONLY skips the transposed weights and changes nothing else, bit for bit."""
+    import torch
+    import mixture_experts_layer_schedule_amd as moe
+    cfg = MID_SIG_CFG
+    inp, ws, _, _, _ = oracle_layer(cfg.with_(backward=True), True)
+    a = gpu_layer(cfg, False, inp=inp, ws=ws)
+    b = gpu_layer(cfg, False, inp=inp, ws=ws, flags=moe.MOE_F_FORWARD_ONLY)
+    assert torch.equal(a.y32, b.y32) and torch.equal(a.y, b.y)
+    for name in ("hq", "hs", "g", "u", "yslot", "perm"):
+        assert torch.equal(a.saved_tensor(name), b.saved_tensor(name)), name

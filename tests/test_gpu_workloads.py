@@ -11,9 +11,14 @@ piece by piece on the same seeded inputs:
   for a near-tie that float32 logits cannot order, and none is expected);
 * x quantisation, bit-exact;
 * the median-load and the maximum-load routed expert (and the shared expert), on up to 384 of
-  their rows (an expert's rows are independent in the forward pass): G/U within the accumulation
-  model, H codes unique-or-admissible, their Y slot rows within 1e-2 RMS + envelope;
-* one sampled token end to end (all its experts): y within 1e-2 RMS + envelope.
+  their rows (an expert's rows are independent in the forward pass), every stage on the GPU's
+  own intermediates (stages.py): quantised weights bit-exact, G and U within 1e-2 RMS, H codes
+  exact outside the float32 slack of a rounding boundary, Y slot rows within 1e-2 RMS;
+* one sampled token: the combine of its Y slots within 1e-2 RMS, and against the oracle's own
+  end-to-end result within 1e-2 RMS + the envelope of code flips (a secondary check).
+
+These workloads are forward-only, so the layer runs with MOE_F_FORWARD_ONLY (no transposed
+weights for a backward pass).
 """
 import numpy as np
 import pytest
@@ -22,6 +27,7 @@ import moe_inputs
 import oracle
 from oracle import envelope
 from oracle.layer import _qdq
+import stages
 from helpers import log, rms, to_np
 
 pytestmark = pytest.mark.gpu
@@ -41,7 +47,7 @@ def run(request):
     cfg = moe_inputs.CONFIGS[request.param]
     log(f"{cfg.name}: inputs and {cfg.E + cfg.n_shared} experts")
     inp = moe_inputs.layer_inputs(cfg, with_dy=False)
-    layer = MoeLayer.from_config(cfg, with_backward=False)
+    layer = MoeLayer.from_config(cfg, with_backward=False, flags=moe.MOE_F_FORWARD_ONLY)
     layer.set_inputs(inp.x_bits, inp.w_r_bits, inp.bias, None)
     layer.load_experts(moe_inputs.iter_expert_weights(cfg, threads=16))
     log(f"{cfg.name}: forward")
@@ -115,42 +121,21 @@ def test_x_quantised_bit_exact(run):
 
 def test_sampled_experts(run):
     cfg, inp, layer, experts = run
-    k, S = cfg.k, cfg.n_shared
-    R = cfg.T * k
-    counts = to_np(layer.saved_tensor("counts"))
-    offs = to_np(layer.saved_tensor("offsets"))
-    perm = to_np(layer.saved_tensor("perm"))
+    v = stages.LayerView(cfg, inp, layer)
+    counts = v.counts
     order = np.argsort(counts[:cfg.E], kind="stable")
-    picks = [int(order[len(order) // 2]), int(order[-1])] + list(range(cfg.E, cfg.E + S))
-    xq, xs = oracle.quantize(inp.x.astype(np.float64), axis=1)
-    X = oracle.dequantize(xq, xs, axis=1)
-    G, U = layer.saved_tensor("g"), layer.saved_tensor("u")
-    ys = layer.saved_tensor("yslot").view(-1, cfg.d)
+    picks = [int(order[len(order) // 2]), int(order[-1])] + list(range(cfg.E, cfg.E + cfg.n_shared))
     rng = np.random.default_rng(0)
+    st = stages.StageStats()
     for e in picks:
-        lo, hi = int(offs[e]), int(offs[e + 1])
+        lo, hi = int(v.offs[e]), int(v.offs[e + 1])
         rows = np.arange(lo, hi)
         if len(rows) > MAX_ROWS:  # rows are independent in the forward pass: check a sorted sample
             rows = np.sort(rng.choice(rows, MAX_ROWS, replace=False))
-        if e < cfg.E:
-            toks = perm[rows] // k
-            slots = toks * (k + S) + perm[rows] % k
-        else:
-            toks = rows - R - (e - cfg.E) * cfg.T
-            slots = toks * (k + S) + k + (e - cfg.E)
-        W1, W2 = experts(e)
         log(f"{cfg.name}: expert {e} ({hi - lo} rows, {len(rows)} checked)")
-        fe = oracle.expert_forward(X[toks], W1, W2)
-        eG, eU, Hlo, Hhi, devH, BY = envelope.expert_forward_envelope(fe, X[toks], W1, W2, EPS)
-        g = to_np(G[rows]).astype(np.float64)
-        u = to_np(U[rows]).astype(np.float64)
-        log(f"  G err / model max {np.max(np.abs(g - fe.G) / eG):.3f}")
-        assert np.all(np.abs(g - fe.G) <= eG) and np.all(np.abs(u - fe.U) <= eU)
-        H = oracle.dequantize(to_np(layer.saved_tensor("hq")[rows]), to_np(layer.saved_tensor("hs")[rows]), axis=1)
-        uniq = Hlo == Hhi
-        log(f"  H codes: {int((~uniq).sum())} of {uniq.size} have two admissible values")
-        assert np.all(H[uniq] == fe.H[uniq]) and np.all((H >= Hlo) & (H <= Hhi))
-        _check(f"Y slot rows of expert {e}", to_np(ys[slots]), fe.Y, BY)
+        w1, w2 = moe_inputs.expert_weights(cfg, e)
+        stages.check_expert_forward(v, e, w1, w2, st, sample=rows)
+    st.report(cfg.name)
 
 
 def test_sampled_token(run):
@@ -163,7 +148,12 @@ def test_sampled_token(run):
     fw = oracle.layer_forward(x, inp.w_r, experts, cfg.k, cfg.score, inp.bias, cfg.n_shared)
     fenv = envelope.forward_envelope(fw, experts, EPS)
     assert np.array_equal(to_np(layer.saved_tensor("idx")[t]), fw.idx[0])
-    _check(f"y[{t}]", to_np(layer.y32[t:t + 1]), fw.y, fenv.By)
+    ys = to_np(layer.saved_tensor("yslot")[t]).astype(np.float64)
+    w = to_np(layer.saved_tensor("w")[t]).astype(np.float64)
+    st = stages.StageStats()
+    st.err(f"y[{t}] from its Y slots", to_np(layer.y32[t]), w @ ys[:cfg.k] + ys[cfg.k:].sum(axis=0))
+    st.report(cfg.name)
+    _check(f"y[{t}] end to end", to_np(layer.y32[t:t + 1]), fw.y, fenv.By)
     # the bf16 output is the float32 one rounded to nearest even
     y16 = to_np(layer.y[t:t + 1].view(torch.int16))
     ref16 = torch.from_numpy(to_np(layer.y32[t:t + 1])).to(torch.bfloat16).view(torch.int16).numpy()

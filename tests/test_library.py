@@ -27,14 +27,37 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, n), n
 
 
+def test_header_structs_match_the_binding():
+    """moe_saved_layout / moe_workspace_layout field order in moe.h equals the ctypes mirrors."""
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    for name, cls in (("moe_saved_layout", moe.moe_saved_layout), ("moe_workspace_layout", moe.moe_workspace_layout)):
+        body = re.search(r"typedef struct %s \{(.*?)\} %s;" % (name, name), text, flags=re.S).group(1)
+        fields = re.findall(r"^\s*size_t\s+(\w+);", body, flags=re.M)
+        assert fields == [f for f, _ in cls._fields_], name
+    body = re.search(r"typedef struct moe_config \{(.*?)\} moe_config;", text, flags=re.S).group(1)
+    fields = re.findall(r"^\s*u?int32_t\s+(\w+);", body, flags=re.M)
+    assert fields == [f for f, _ in moe.moe_config._fields_]
+
+
 def test_query_layout_is_aligned_and_ordered():
     cfg = moe.make_config(256, 256, 8, 2, 128)
-    ws, sl = moe.moe_query(cfg)
-    offs = [getattr(sl, f) for f, _ in moe.moe_saved_layout._fields_]
-    assert all(o % 256 == 0 for o in offs[:-1])
-    assert offs == sorted(offs)
-    assert sl.yslot + 4 * 256 * 2 * 256 <= sl.total
-    assert ws > 0
+    ws, sl, wl = moe.moe_query(cfg, with_workspace_layout=True)
+    for layout in (sl, wl):
+        offs = [getattr(layout, f) for f, _ in type(layout)._fields_ if f not in ("tok_stride",)]
+        assert all(o % 256 == 0 for o in offs[:-1])
+        assert offs == sorted(offs)
+    assert sl.yslot + 4 * 256 * 2 * 256 <= sl.w1t
+    # transposed weights: NX * 2I * d codes (+ scales) for W1t, half of that for W2t
+    assert sl.w1ts - sl.w1t >= 8 * 2 * 128 * 256 and sl.w2ts - sl.w2t >= 8 * 128 * 256
+    assert ws == wl.total and ws > 0
+    assert wl.tok_stride % 128 == 0 and wl.tok_stride >= 256 * 2 + 127 * 8
+
+
+def test_forward_only_layout_drops_transposed_weights():
+    _, full = moe.moe_query(moe.make_config(256, 256, 8, 2, 128))
+    _, fo = moe.moe_query(moe.make_config(256, 256, 8, 2, 128, flags=moe.MOE_F_FORWARD_ONLY))
+    assert fo.w1t == fo.w1ts == fo.w2t == fo.w2ts == fo.total
+    assert fo.total < full.total
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -46,11 +69,19 @@ def test_query_layout_is_aligned_and_ordered():
     (dict(n_shared=2), moe.MOE_ESHAPE),
     (dict(score_fn=7), moe.MOE_EINVAL),
     (dict(T=0), moe.MOE_ESHAPE),
-    (dict(ring_rows=128), moe.MOE_ESHAPE),   # ring slots hold 256 rows
-    (dict(chunk_rows=128), moe.MOE_ESHAPE),
-    (dict(producer_wgs=129), moe.MOE_ESHAPE),
+    (dict(ring_rows=256), moe.MOE_EINVAL),   # tuning knobs only act on the ring dispatch
+    (dict(chunk_rows=256), moe.MOE_EINVAL),
+    (dict(producer_wgs=8), moe.MOE_EINVAL),
+    (dict(flags=2), moe.MOE_EINVAL),         # ring dispatch is disabled
     (dict(flags=3), moe.MOE_EINVAL),         # direct gather and ring dispatch together
-    (dict(flags=16), moe.MOE_EINVAL),        # unknown flag
+    (dict(flags=32), moe.MOE_EINVAL),        # unknown flag
+    # 32-bit operand offsets: T * d reaches 2^32
+    (dict(T=(1 << 32) // 7168 + 1, d=7168, E=8, k=1, inter=128), moe.MOE_ESHAPE),
+    # one expert's weights 2 * I * d reach 2^32
+    (dict(d=65536, inter=32768), moe.MOE_ESHAPE),
+    # token-axis operand stride reaches 2^24 (T * k + 127 * E)
+    (dict(T=1 << 20, d=128, E=16, k=16, inter=128), moe.MOE_ESHAPE),
+    (dict(T=1 << 26, d=128, E=16, k=16, inter=128), moe.MOE_ESHAPE),  # T * k >= 2^30
 ])
 def test_query_rejects_bad_config(kw, status):
     base = dict(T=256, d=256, E=8, k=2, inter=128)
@@ -62,9 +93,15 @@ def test_query_rejects_bad_config(kw, status):
     assert ei.value.status == status
 
 
-@pytest.mark.parametrize("flags", [0, 1, 4, 5, 8, 9])
+def test_query_accepts_sizes_just_inside_the_limits():
+    moe.moe_query(moe.make_config((1 << 32) // 7168, 7168, 8, 1, 128))       # T * d < 2^32
+    moe.moe_query(moe.make_config(256, 65536, 8, 2, 32768 - 128))             # 2 I d < 2^32
+    moe.moe_query(moe.make_config(1 << 19, 128, 16, 16, 128))                 # stride < 2^24
+
+
+@pytest.mark.parametrize("flags", [0, 1, 4, 5, 8, 9, 16, 20])
 def test_query_accepts_schedule_flags(flags):
-    """Direct gather (1) and the launch-order backward (4) are valid alone and together."""
+    """Direct gather (1), the launch-order backward (4), identity experts (8) and forward only (16)."""
     ws, _ = moe.moe_query(moe.make_config(256, 256, 8, 2, 128, flags=flags))
     assert ws > 0
 
@@ -72,15 +109,40 @@ def test_query_accepts_schedule_flags(flags):
 def test_forward_rejects_null_and_misaligned_pointers_without_launching():
     cfg = moe.make_config(256, 256, 8, 2, 128)
     with pytest.raises(moe.MoeError) as ei:
-        moe.moe_fwd(cfg, 0, 0, None, 0, 0, 0, 0, 0, None, 0, 0, stream=0)
+        moe.moe_fwd(cfg, 0, 0, None, 0, 0, 0, 0, 0, None, 0, 0, stream=0, saved_bytes=0, workspace_bytes=0)
     assert ei.value.status == moe.MOE_EINVAL
+    big = 1 << 40
     with pytest.raises(moe.MoeError) as ei:
-        moe.moe_fwd(cfg, 4096 + 8, 4096, None, 4096, 4096, 4096, 4096, 4096, None, 4096, 4096, stream=0)
+        moe.moe_fwd(cfg, 4096 + 8, 4096, None, 4096, 4096, 4096, 4096, 4096, None, 4096, 4096, stream=0,
+                    saved_bytes=big, workspace_bytes=big)
     assert ei.value.status == moe.MOE_EALIGN
     bad = moe.make_config(256, 100, 8, 2, 128)
     with pytest.raises(moe.MoeError) as ei:
-        moe.moe_bwd(bad, 4096, 4096, 4096, 4096, 4096, 4096, 4096, 4096, 4096, None, 4096, 4096, 4096, 4096, stream=0)
+        moe.moe_bwd(bad, 4096, 4096, 4096, 4096, 4096, None, 4096, 4096, 4096, 4096, stream=0, saved_bytes=big,
+                    workspace_bytes=big)
     assert ei.value.status == moe.MOE_ESHAPE
+
+
+def test_small_buffers_are_rejected_before_any_launch():
+    cfg = moe.make_config(256, 256, 8, 2, 128)
+    ws, sl = moe.moe_query(cfg)
+    p = 1 << 20  # aligned dummy addresses: the call must return before touching them
+    for sb, wb in ((sl.total - 1, ws), (sl.total, ws - 1), (0, 0)):
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_fwd(cfg, p, p, None, p, p, p, p, p, None, p, p, stream=0, saved_bytes=sb, workspace_bytes=wb)
+        assert ei.value.status == moe.MOE_EWORKSPACE
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_bwd(cfg, p, p, p, p, p, None, p, p, p, p, stream=0, saved_bytes=sb, workspace_bytes=wb)
+        assert ei.value.status == moe.MOE_EWORKSPACE
+
+
+@pytest.mark.parametrize("flags", [moe.MOE_F_IDENTITY_EXPERTS, moe.MOE_F_FORWARD_ONLY])
+def test_backward_rejects_forward_only_modes(flags):
+    cfg = moe.make_config(256, 256, 8, 2, 128, flags=flags)
+    p, big = 1 << 20, 1 << 40
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_bwd(cfg, p, p, p, p, p, None, p, p, p, p, stream=0, saved_bytes=big, workspace_bytes=big)
+    assert ei.value.status == moe.MOE_EINVAL
 
 
 def test_quantize_rejects_ragged_blocks():
@@ -95,3 +157,4 @@ def test_quantize_rejects_ragged_blocks():
 def test_strerror_covers_every_status():
     for s in range(7):
         assert moe.moe_strerror(s) and moe.moe_strerror(s) != "unknown status"
+    assert moe.moe_strerror(99) == "unknown status"
