@@ -135,9 +135,10 @@ typedef struct moe_saved_layout {
   size_t hs;         /* e8m0  [RS, I/32] */
   size_t yslot;      /* float [T, k + S, d] expert output of every (token, slot) */
   size_t w1t;        /* fp8   [NX, d, 2I]  W1 transposed, requantised along 2I (experts with rows) */
-  size_t w1ts;       /* e8m0  [NX, d, 2I/32] */
+  size_t w1ts;       /* e8m0  [NX, 2I/128, d, 4]  its scales, word-major: [e][q][k][b] is the
+                        scale of block 4q + b of transposed row k */
   size_t w2t;        /* fp8   [NX, I, d]   W2 transposed, requantised along d (experts with rows) */
-  size_t w2ts;       /* e8m0  [NX, I, d/32] */
+  size_t w2ts;       /* e8m0  [NX, d/128, I, 4]  its scales, word-major as for w1ts */
   size_t total;      /* bytes of `saved` */
 } moe_saved_layout;
 

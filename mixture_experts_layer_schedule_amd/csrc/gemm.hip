@@ -61,15 +61,16 @@ __global__ __launch_bounds__(512, 1) void k_gemm_gateup(GateUpArgs p) {
   const uint8_t* w1 = p.w1q + (size_t)rt.e * 2 * I * d;
   const uint8_t* w1s = p.w1s + (size_t)rt.e * 2 * I * (d / 32);
   const int last = rt.rows - 1;
-  // transposed weight W1t[e] [d][2I]: staged row block w (32 rows) holds gate rows
-  // n0 + 32(w / 2) .. (w even) or the matching up rows (w odd)
-  const int wv = threadIdx.x >> 6;
-  uint8_t* w1t = p.w1t ? p.w1t + (size_t)rt.e * d * 2 * I : nullptr;
-  uint8_t* w1ts = p.w1t ? p.w1ts + (size_t)rt.e * d * (2 * I / 32) : nullptr;
-  const int orow = (wv & 1 ? I : 0) + n0 + 32 * (wv >> 1);
-  auto after = [=](const uint8_t* st, int t) __attribute__((always_inline)) {
-    if (w1t && t % rt.nm == rt.m) requant_stage_t8(st, t * KS, orow, w1t, w1ts, 2 * I);
-  };
+  // transposed weight W1t[e] [d][2I]: half 0 of the tile is gate rows n0 .. n0 + 128, half 1
+  // the up rows I + n0 ..
+  RequantT8<true> side;
+  side.wt = p.w1t ? p.w1t + (size_t)rt.e * d * 2 * I : nullptr;
+  side.wts = p.w1t ? p.w1ts + (size_t)rt.e * d * (2 * I / 32) : nullptr;
+  side.ldt = 2 * I;
+  side.K = d;
+  side.obase = ((threadIdx.x >> 8) ? I : 0) + n0;
+  side.m = rt.m;
+  side.nm = rt.nm;
   dispatch_rows(rt.rows, [&]<int F>() {
     TileLoads8<F> L;
     L.init(p.xq, [&](int r) { return p.xq + (size_t)row_token(s, rt.r0 + min(r, last)) * d; },
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_gateup(GateUpArgs p) {
            p.xs, [&](int r) { return p.xs + (size_t)row_token(s, rt.r0 + min(r, last)) * (d / 32); },
            w1s, [&](int r) { return w1s + (size_t)gateup_brow(r, n0, I) * (d / 32); });
     v16f acc[(F + 1) / 2][2];
-    mainloop8<F>(lds, L, d / KS, acc, after);
+    mainloop8<F>(lds, L, d / KS, acc, side);
     gateup_epilogue8<F>(acc, rt.r0, rt.rows, n0, I, p.g, p.u, p.hq, p.hs);
   });
 }
@@ -100,13 +101,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_down(DownArgs p) {
   const int last = rt.rows - 1;
   const int w = threadIdx.x >> 6, l = lane_id(), i = l & 31, h = l >> 5, wc = w & 3;
   const bool active = n0 + 64 * wc < d;
-  // transposed weight W2t[e] [I][d]: staged row block w holds W2 rows n0 + 32w .. (none past d)
-  uint8_t* w2t = p.w2t ? p.w2t + (size_t)rt.e * I * d : nullptr;
-  uint8_t* w2ts = p.w2t ? p.w2ts + (size_t)rt.e * I * (d / 32) : nullptr;
-  const int orow = n0 + 32 * w < d ? n0 + 32 * w : -1;
-  auto after = [=](const uint8_t* st, int t) __attribute__((always_inline)) {
-    if (w2t && t % rt.nm == rt.m) requant_stage_t8(st, t * KS, orow, w2t, w2ts, d);
-  };
+  // transposed weight W2t[e] [I][d]: half h of the tile is W2 rows n0 + 128h .. (none past d)
+  RequantT8<false> side;
+  side.wt = p.w2t ? p.w2t + (size_t)rt.e * I * d : nullptr;
+  side.wts = p.w2t ? p.w2ts + (size_t)rt.e * I * (d / 32) : nullptr;
+  side.ldt = d;
+  side.K = I;
+  side.obase = n0 + 128 * (w >> 2) < d ? n0 + 128 * (w >> 2) : -1;
+  side.m = rt.m;
+  side.nm = rt.nm;
   dispatch_rows(rt.rows, [&]<int F>() {
     constexpr int FH = (F + 1) / 2;
     const int m0 = (w >> 2) * FH;
@@ -118,7 +121,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_down(DownArgs p) {
            hsa, [&](int r) { return hsa + (size_t)min(r, last) * (I / 32); },
            w2s, [&](int r) { return w2s + (size_t)min(n0 + r, d - 1) * (I / 32); });
     v16f acc[FH][2];
-    mainloop8<F>(lds, L, I / KS, acc, after);
+    mainloop8<F>(lds, L, I / KS, acc, side);
     const int64_t* slot = row_slot_table(s, rt, lds + ((I / KS) % kStages) * STAGE_BYTES);
     if (!active) return;
     static_for<FH>([&]<int m>() {
@@ -152,14 +155,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_down(DgradDownArgs p) {
   const int last = rt.rows - 1;
   const int w = threadIdx.x >> 6, l = lane_id(), i = l & 31, h = l >> 5;
   const bool active = n0 + 64 * w < I;
-  const uint8_t* w2t = p.w2t + (size_t)rt.e * I * d;  // W2^T [I][d], quantised along d
+  const uint8_t* w2t = p.w2t + (size_t)rt.e * I * d;  // W2^T [I][d], quantised along d; scales [d/128][I] words
   const uint8_t* w2ts = p.w2ts + (size_t)rt.e * I * (d / 32);
   dispatch_rows(rt.rows, [&]<int F>() {
     TileLoads<F> L;
     L.init(p.dyq, [&](int r) { return p.dyq + (size_t)row_token(s, rt.r0 + min(r, last)) * d; },
            w2t, [&](int r) { return w2t + (size_t)min(n0 + r, I - 1) * d; },
            p.dys, [&](int r) { return p.dys + (size_t)row_token(s, rt.r0 + min(r, last)) * (d / 32); },
-           w2ts, [&](int r) { return w2ts + (size_t)min(n0 + r, I - 1) * (d / 32); });
+           w2ts, [&](int r) { return w2ts + (size_t)min(n0 + r, I - 1) * 4; });
+    L.bsk = 4 * I;  // word-major scales: stage t's words are plane t
     v16f acc[F][2];
     mainloop<F, 2>(lds, L, d / KS, acc);
     // combine weight of every row of the tile, once, through LDS
@@ -226,7 +230,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_gateup(DgradGateUpArgs p)
   const int last = rt.rows - 1;
   const int w = threadIdx.x >> 6, l = lane_id(), i = l & 31, h = l >> 5;
   const bool active = n0 + 64 * w < d;
-  const uint8_t* w1t = p.w1t + (size_t)rt.e * d * I2;  // W1^T [d][2I], quantised along 2I
+  const uint8_t* w1t = p.w1t + (size_t)rt.e * d * I2;  // W1^T [d][2I], quantised along 2I; scales [2I/128][d] words
   const uint8_t* w1ts = p.w1ts + (size_t)rt.e * d * (I2 / 32);
   dispatch_rows(rt.rows, [&]<int F>() {
     TileLoads<F> L;
@@ -235,7 +239,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_gateup(DgradGateUpArgs p)
     L.init(ga, [&](int r) { return ga + (size_t)min(r, last) * I2; },
            w1t, [&](int r) { return w1t + (size_t)min(n0 + r, d - 1) * I2; },
            gsa, [&](int r) { return gsa + (size_t)min(r, last) * (I2 / 32); },
-           w1ts, [&](int r) { return w1ts + (size_t)min(n0 + r, d - 1) * (I2 / 32); });
+           w1ts, [&](int r) { return w1ts + (size_t)min(n0 + r, d - 1) * 4; });
+    L.bsk = 4 * d;  // word-major scales: stage t's words are plane t
     v16f acc[F][2];
     mainloop<F, 2>(lds, L, I2 / KS, acc);
     const int64_t* slot = row_slot_table(s, rt, lds + ((I2 / KS) % kStages) * STAGE_BYTES);

@@ -200,11 +200,12 @@ MOE_DEV void issue_stage(const TileLoads<F>& L, uint8_t* lds, int t) {
   static_for<8>([&]<int u>() { lds_load16<0>(L.bbase + (L.b[u] + kb), st + A_STAGE + 1024 * (w + 4 * u)); });
 }
 
-// Wait until at most N of this wave's loads are outstanding, then meet the other waves.  The
-// wait and the barrier are one statement so that no LDS access moves across either.
+// Wait until at most N of this wave's memory operations are outstanding (and its LDS reads have
+// returned), then meet the other waves.  The wait and the barrier are one statement so that no
+// LDS access moves across either.
 template <int N>
 MOE_DEV void wait_loads_and_sync() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 // An empty statement that reads and rewrites two accumulator tiles in place: code after it
@@ -384,10 +385,6 @@ MOE_DEV void compute_stage8(const uint8_t* st, v16f (&acc)[(F + 1) / 2][2]) {
   });
 }
 
-struct NoAfterStage {
-  MOE_DEV void operator()(const uint8_t*, int) const {}
-};
-
 // An empty statement that reads and rewrites the accumulators in place: code after it cannot
 // start before the matrix instructions that produce them have been issued.
 MOE_DEV void pin_vgprs(v16f& a, v16f& b) { asm volatile("" : "+v"(a), "+v"(b)::"memory"); }
@@ -396,12 +393,22 @@ MOE_DEV void pin_acc(v16f (&acc)[FH][2]) {
   static_for<FH>([&]<int m>() { pin_vgprs(acc[m][0], acc[m][1]); });
 }
 
-// acc = this wave's part of A_tile * B_tile^T over K = 128 nk; one barrier per stage.  After the
-// matrix instructions of stage t the workgroup calls after_stage(staged buffer, t): vector work
-// on the stage that is still resident (the next barrier retires the buffer).
-template <int F, class AfterStage>
+struct NoSideWork {
+  static constexpr bool kEnabled = false;
+  MOE_DEV bool wants(int) const { return false; }
+  MOE_DEV void run(const uint8_t*, int) {}
+};
+
+// acc = this wave's part of A_tile * B_tile^T over K = 128 nk; one barrier per stage.
+//
+// Optional side work on the streamed stages (the transposed weight requantisation): once stage
+// t has landed and the loads of stage t + 1 are issued, the wave does the side work on stage t
+// (side.run, when side.wants(t)) and then multiplies stage t.  Its stores thus follow the loads
+// of stage t + 1 in issue order and retire while the matrix work runs, so the wait at the top of
+// the next iteration (a wave's memory counter retires in issue order) is not lengthened by them.
+template <int F, class Side = NoSideWork>
 MOE_DEV void mainloop8(uint8_t* lds, const TileLoads8<F>& L, int nk, v16f (&acc)[(F + 1) / 2][2],
-                       const AfterStage& after_stage) {
+                       Side&& side = Side{}) {
   static_for<(F + 1) / 2>([&]<int m>() {
     acc[m][0] = (v16f){};
     acc[m][1] = (v16f){};
@@ -411,20 +418,14 @@ MOE_DEV void mainloop8(uint8_t* lds, const TileLoads8<F>& L, int nk, v16f (&acc)
   for (int t = 0; t < nk; ++t) {
     wait_loads_and_sync<0>();  // stage t has landed; every wave is done with stage t - 1
     if (t + 1 < nk) issue_stage8<F>(L, lds, t + 1);
-    compute_stage8<F>(lds + (t % 2) * STAGE_BYTES, acc);
-    if constexpr (!std::is_same_v<AfterStage, NoAfterStage>) {
-      // an empty statement that rewrites the accumulators: the stage's matrix instructions
-      // issue before the vector work below (a branch there would otherwise let the compiler
-      // sink them past it, keeping every A/B fragment live across the vector work)
+    if constexpr (std::remove_reference_t<Side>::kEnabled) {
+      // the previous stage's matrix instructions are issued before the side work (a branch
+      // could otherwise let the compiler sink them past it)
       pin_acc<(F + 1) / 2>(acc);
-      after_stage((const uint8_t*)(lds + (t % 2) * STAGE_BYTES), t);
+      if (side.wants(t)) side.run((const uint8_t*)(lds + (t % 2) * STAGE_BYTES), t);
     }
+    compute_stage8<F>(lds + (t % 2) * STAGE_BYTES, acc);
   }
-}
-
-template <int F>
-MOE_DEV void mainloop8(uint8_t* lds, const TileLoads8<F>& L, int nk, v16f (&acc)[(F + 1) / 2][2]) {
-  mainloop8<F>(lds, L, nk, acc, NoAfterStage{});
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -438,71 +439,111 @@ MOE_DEV void mainloop8(uint8_t* lds, const TileLoads8<F>& L, int nk, v16f (&acc)
 // whole 32-row blocks of 128 columns, so the transposed codes are produced there and written
 // to HBM once (no separate pass that reads the weights again).
 //
-// Wave w takes staged rows [32w, 32w + 32) (one block along the requantisation axis): lane l
-// reads rows 32w + 4(l >> 3) .. + 4 at 16-byte chunk l & 7 (columns 16(l & 7) .. + 16) and the
-// four rows' scale bytes; the block maximum of a column spans the 8 lanes l ^ 8, l ^ 16, l ^ 32
-// (a row rotation, then the two lane-swap instructions).  A lane then writes its 4 codes of
-// each column as one 4-byte word of the transposed row and 2 of the 16 columns' scale bytes.
-//   wt  [K][ldt] codes, wts [K][ldt / 32] scales: transposed weight of the expert;
-//   k0: first K index (column of the weight) of the stage; orow: first transposed-row index
-//   of staged row block w, or -1 to skip the block.
-MOE_DEV void requant_stage_t8(const uint8_t* st, int k0, int orow, uint8_t* wt, uint8_t* wts, int ldt) {
-  const int w = threadIdx.x >> 6, l = lane_id();
-  const int g = l & 7, rq = l >> 3;
-  if (orow < 0) return;  // wave-uniform
-  // opaque per call: keeps the compiler from hoisting the 16 columns' addresses out of the GEMM's
-  // K loop, where they would stay live (and spill) across the matrix work
-  asm volatile("" : "+s"(ldt), "+s"(wt), "+s"(wts));
-  const int r0 = 32 * w + 4 * rq;
-  v4i raw[4];
-  float f[4];
-  __builtin_amdgcn_sched_barrier(0);  // after the stage's matrix instructions
-  static_for<4>([&]<int j>() {
-    const int r = r0 + j;
-    raw[j] = *(const v4i*)(st + A_STAGE + r * KS + 16 * (g ^ swz(r)));
-    f[j] = e8m0_scale(st[DATA_BYTES + TM * 4 + 4 * r + (g >> 1)]);
-  });
-  const size_t col0 = (size_t)(k0 + 16 * g);
-  uint8_t* out = wt + col0 * ldt + orow + 4 * rq;
-  // four quarters of 4 columns: word P of every row piece holds columns 4P .. 4P + 3 (few
-  // registers live at a time: this runs inside the GEMM's main loop)
-  uint32_t sbytes[4];  // the 16 columns' scale bytes, byte c % 4 of word c / 4 (same in the 8 lanes)
-  static_for<4>([&]<int P>() {
-    float v[4][4];
-    static_for<4>([&]<int j>() {
-      const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(raw[j][P], false);
-      const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(raw[j][P], true);
-      v[j][0] = lo[0] * f[j];
-      v[j][1] = lo[1] * f[j];
-      v[j][2] = hi[0] * f[j];
-      v[j][3] = hi[1] * f[j];
+// The tile's 256 weight rows form two halves of 128 rows that are contiguous in the transposed
+// weight (gate rows n0 .. n0 + 128 and up rows I + n0 .. of W1; W2 rows n0 .. n0 + 128 and
+// n0 + 128 .. n0 + 256).  Wave w takes half w / 4 and stage columns 32 (w % 4) .. + 32, in two
+// passes of 16; lane l reads 8 rows 8 (l % 16) .. + 8 of the half at 4 columns 4 (l / 16) .. + 4
+// of the pass (a 4-byte piece of each row) and the rows' scale bytes.  A 32-row block is held by
+// the 4 lanes l ^ 1, l ^ 2, l ^ 3.  The hardware's scaled conversions decode a code pair times
+// the row's scale and encode a value pair divided by the new scale (round to nearest even), so
+// a value costs about four vector instructions.  Each column's 8 codes of a lane are one 8-byte
+// store, and the 16 lanes that share a column write its 128 contiguous transposed bytes in one
+// instruction: whole cache lines, written once.  The scales are stored word-major: transposed
+// row k's blocks 4q .. 4q + 3 form word q of plane [q][k], which is the word a dgrad stage loads
+// per row, and a wave's 16 columns of a pass write 64 contiguous bytes.
+
+// e8m0 byte -> the float 2^(byte - 127) that the scaled conversions take (byte 0 is 2^-127:
+// the instructions read the exponent field only).
+MOE_DEV float e8m0_operand(uint32_t byte) { return __uint_as_float(byte << 23); }
+
+// kGateUp: the staged rows of a gate/up tile alternate 32 gate and 32 up rows per wave; the
+// down GEMM's are the weight rows in order.
+template <bool kGateUp>
+struct RequantT8 {
+  static constexpr bool kEnabled = true;
+  uint8_t* wt;   // [K][ldt] transposed codes of the expert (NULL: no requantisation)
+  uint8_t* wts;  // [ldt / 128][K] words of 4 scale bytes (blocks 4q .. 4q + 3 of transposed row k)
+  int ldt;       // transposed row length (the requantisation axis)
+  int K;         // transposed rows (the forward GEMM's reduction axis)
+  int obase;     // transposed-row index of row 0 of this wave's half, or -1 to skip the half
+  int m, nm;     // stage t is requantised by the item with t % nm == m
+
+  MOE_DEV bool wants(int t) const { return wt != nullptr && t % nm == m; }
+
+  // staged row of row x (0 .. 127) of half hf
+  static MOE_DEV int staged(int hf, int x) {
+    return kGateUp ? 64 * (x >> 5) + 32 * hf + (x & 31) : 128 * hf + x;
+  }
+
+  // requantise staged stage t (K columns [128t, 128t + 128)) and store it
+  MOE_DEV void run(const uint8_t* st, int t) {
+    if (obase < 0) return;  // wave-uniform
+    const int w = threadIdx.x >> 6, l = lane_id();
+    const int hf = w >> 2, cq = w & 3, rg = l & 15, cgp = l >> 4;
+    // the lane's 8 rows are staged rows r0 .. r0 + 8 (a multiple of 8: they share swz's high part)
+    const int r0 = staged(hf, 8 * rg);
+    float f[8];  // the rows' scales as conversion operands (one K block per wave: block cq)
+    static_for<8>([&]<int j>() { f[j] = e8m0_operand(st[DATA_BYTES + TM * 4 + 4 * (r0 + j) + cq]); });
+    int ld = ldt;
+    // opaque per call: keeps the compiler from hoisting the columns' addresses out of the GEMM's
+    // K loop, where they would stay live (and spill) across the matrix work
+    asm volatile("" : "+s"(ld));
+    static_for<2>([&]<int pass>() {
+      const int c16 = 32 * cq + 16 * pass + 4 * cgp;  // first stage column of the lane
+      uint32_t raw[8];
+      const uint8_t* rp = st + A_STAGE + r0 * KS + (c16 & 15);
+      const int x = ((c16 >> 4) ^ (r0 >> 3)) & 7;  // chunk slot of row r0 + j is x ^ j (swz)
+      static_for<8>([&]<int j>() { raw[j] = *(const uint32_t*)(rp + j * KS + 16 * (x ^ j)); });
+      const size_t col0 = (size_t)(KS * t + c16);
+      uint8_t* out = wt + col0 * ld + obase + 8 * rg;
+      uint8_t* sout = wts + ((size_t)(obase >> 7) * K + col0) * 4 + (rg >> 2);
+      // two column pairs: byte pair P of every row's piece
+      static_for<2>([&]<int P>() {
+        float v[8][2];
+        static_for<8>([&]<int j>() {
+          const v2f x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(raw[j], f[j], P != 0);
+          v[j][0] = x[0];
+          v[j][1] = x[1];
+        });
+        static_for<2>([&]<int c>() {
+          float mx = fabsf(v[0][c]);
+          static_for<7>([&]<int j>() { mx = fmaxf(mx, fabsf(v[j + 1][c])); });
+          // non-negative floats order like their bit patterns: the lane maxima cross as integers
+          uint32_t u = __float_as_uint(mx);
+          u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, false));  // l ^ 1
+          u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, false));  // l ^ 2
+          const uint32_t byte = e8m0_from_amax(__uint_as_float(u));
+          const float sc = e8m0_operand(byte);
+          // the encode saturates values above 448 except one: exactly 480 (mantissa 1.875 in
+          // the top binade, the block maximum in about one column in eight) comes out as the
+          // NaN pattern 0x7F (measured on the device), so values are clamped to
+          // +-448 x 2^(byte - 127)
+          const float lim = 1.75f * __uint_as_float((byte + 8) << 23);
+          typedef short v2s __attribute__((ext_vector_type(2)));
+          v2i codes;
+          static_for<2>([&]<int q>() {
+            v2s wv = {0, 0};
+            wv = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(wv, __builtin_amdgcn_fmed3f(v[4 * q][c], -lim, lim),
+                                                          __builtin_amdgcn_fmed3f(v[4 * q + 1][c], -lim, lim), sc,
+                                                          false);
+            wv = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(wv, __builtin_amdgcn_fmed3f(v[4 * q + 2][c], -lim, lim),
+                                                          __builtin_amdgcn_fmed3f(v[4 * q + 3][c], -lim, lim), sc,
+                                                          true);
+            codes[q] = __builtin_bit_cast(int, wv);
+          });
+          constexpr int col = 2 * P + c;
+          // non-temporal: the forward pass never reads these back, so they stream past the
+          // caches instead of evicting the weight slices and rows the neighbouring tiles reuse
+          __builtin_nontemporal_store(codes, (v2i*)(out + (size_t)col * ld));
+          // the 4 lanes of a block store its scale byte (the same value): the words of the 16
+          // columns of a pass are contiguous, so the bytes of a line meet in L2 at once
+          sout[4 * col] = (uint8_t)byte;
+        });
+        __builtin_amdgcn_sched_barrier(0);  // one pair's values live at a time
+      });
     });
-    sbytes[P] = 0;
-    static_for<4>([&]<int c>() {
-      const float m = fmaxf(fmaxf(fabsf(v[0][c]), fabsf(v[1][c])), fmaxf(fabsf(v[2][c]), fabsf(v[3][c])));
-      // non-negative floats order like their bit patterns: the lane maxima cross as integers
-      uint32_t u = __float_as_uint(m);
-      u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x128, 0xF, 0xF, false));  // l ^ 8
-      const auto p16 = __builtin_amdgcn_permlane16_swap((int)u, (int)u, false, false);        // l ^ 16
-      u = max((uint32_t)p16[0], (uint32_t)p16[1]);
-      const auto p32 = __builtin_amdgcn_permlane32_swap((int)u, (int)u, false, false);        // l ^ 32
-      u = max((uint32_t)p32[0], (uint32_t)p32[1]);
-      const uint32_t byte = e8m0_from_amax(__uint_as_float(u));
-      const float inv = e8m0_inv_scale(byte);
-      const uint32_t codes = pack4_e4m3(v[0][c] * inv, v[1][c] * inv, v[2][c] * inv, v[3][c] * inv);
-      *(uint32_t*)(out + (size_t)(4 * P + c) * ldt) = codes;
-      sbytes[P] |= byte << (8 * c);
-    });
-    __builtin_amdgcn_sched_barrier(0);  // one quarter's values live at a time
-  });
-  // lane (g, rq) stores the scale bytes of columns rq and rq + 8 (no branch)
-  const uint32_t sh = 8 * (rq & 3);
-  const uint32_t lo = (rq & 4) ? sbytes[1] : sbytes[0];
-  const uint32_t hi = (rq & 4) ? sbytes[3] : sbytes[2];
-  uint8_t* sp = wts + (col0 + rq) * (ldt / 32) + orow / 32;
-  sp[0] = (uint8_t)(lo >> sh);
-  sp[(size_t)8 * (ldt / 32)] = (uint8_t)(hi >> sh);
-}
+  }
+};
 
 // Quantise 32 consecutive columns of one row held by the 32 lanes of a half-wave:
 // returns this lane's code; *scale receives the block's e8m0 byte.

@@ -23,7 +23,7 @@ struct GateUpArgs {
   const uint8_t *xq, *xs, *w1q, *w1s;
   float *g, *u;
   uint8_t *hq, *hs;
-  uint8_t *w1t, *w1ts;  // [NX][d][2I] + [NX][d][2I/32]: W1 transposed, requantised along 2I (NULL: skip)
+  uint8_t *w1t, *w1ts;  // [NX][d][2I] + [NX][2I/128][d][4]: W1 transposed, requantised along 2I (NULL: skip)
   int d, I;
 };
 
@@ -31,14 +31,14 @@ struct DownArgs {
   SchedView s;
   const uint8_t *hq, *hs, *w2q, *w2s;
   float* yslot;
-  uint8_t *w2t, *w2ts;  // [NX][I][d] + [NX][I][d/32]: W2 transposed, requantised along d (NULL: skip)
+  uint8_t *w2t, *w2ts;  // [NX][I][d] + [NX][d/128][I][4]: W2 transposed, requantised along d (NULL: skip)
   int d, I;
 };
 
 struct DgradDownArgs {
   SchedView s;
   const uint8_t *dyq, *dys;
-  const uint8_t *w2t, *w2ts;  // [NX][I][d] + [NX][I][d/32] (written by the forward down GEMM)
+  const uint8_t *w2t, *w2ts;  // [NX][I][d] + [NX][d/128][I][4] (written by the forward down GEMM)
   const float *w, *g, *u;
   uint8_t *dguq, *dgus;
   int d, I;
@@ -47,7 +47,7 @@ struct DgradDownArgs {
 struct DgradGateUpArgs {
   SchedView s;
   const uint8_t *dguq, *dgus;
-  const uint8_t *w1t, *w1ts;  // [NX][d][2I] + [NX][d][2I/32] (written by the forward gate/up GEMM)
+  const uint8_t *w1t, *w1ts;  // [NX][d][2I] + [NX][2I/128][d][4] (written by the forward gate/up GEMM)
   float* dxslot;
   int d, I;
 };

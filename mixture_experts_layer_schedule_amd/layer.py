@@ -101,8 +101,8 @@ class MoeLayer:
             "g": (torch.float32, (RS, I)), "u": (torch.float32, (RS, I)),
             "hq": (torch.uint8, (RS, I)), "hs": (torch.uint8, (RS, I // 32)),
             "yslot": (torch.float32, (T, k + S, d)),
-            "w1t": (torch.uint8, (NX, d, 2 * I)), "w1ts": (torch.uint8, (NX, d, 2 * I // 32)),
-            "w2t": (torch.uint8, (NX, I, d)), "w2ts": (torch.uint8, (NX, I, d // 32)),
+            "w1t": (torch.uint8, (NX, d, 2 * I)), "w1ts": (torch.uint8, (NX, 2 * I // 128, d, 4)),
+            "w2t": (torch.uint8, (NX, I, d)), "w2ts": (torch.uint8, (NX, d // 128, I, 4)),
         }
         dt, shape = spec[name]
         off = getattr(self.layout, name)

@@ -15,6 +15,7 @@ import torch
 import moe_inputs
 import oracle
 from oracle.layer import _qdq
+from stages import word_major
 
 
 def _t(a, dtype=None):
@@ -47,9 +48,9 @@ class FakeLayer:
         self.w2q = _t(np.stack([a[2] for a in q]))
         self.w2s = _t(np.stack([a[3] for a in q]))
         w1t = np.zeros((NX, d, 2 * I), np.uint8)
-        w1ts = np.zeros((NX, d, 2 * I // 32), np.uint8)
+        w1ts = np.zeros((NX, 2 * I // 128, d, 4), np.uint8)
         w2t = np.zeros((NX, I, d), np.uint8)
-        w2ts = np.zeros((NX, I, d // 32), np.uint8)
+        w2ts = np.zeros((NX, d // 128, I, 4), np.uint8)
         g = np.zeros((RS, I), f32)
         u = np.zeros((RS, I), f32)
         hq = np.zeros((RS, I), np.uint8)
@@ -71,7 +72,7 @@ class FakeLayer:
             a = q[e]
             q1t, s1t = oracle.requantize(a[0], a[1], from_axis=1, to_axis=0)
             q2t, s2t = oracle.requantize(a[2], a[3], from_axis=1, to_axis=0)
-            w1t[e], w1ts[e], w2t[e], w2ts[e] = q1t.T, s1t.T, q2t.T, s2t.T
+            w1t[e], w1ts[e], w2t[e], w2ts[e] = q1t.T, word_major(s1t), q2t.T, word_major(s2t)
             fe, be = fw.experts[e], bw.experts[e]
             g[lo:hi], u[lo:hi] = fe.G, fe.U
             hq[lo:hi], hs[lo:hi] = fe.Hq, fe.Hs

@@ -73,6 +73,13 @@ def name_frac(n):
     return f"{n}: too many codes on the other side of a rounding boundary"
 
 
+def word_major(st):
+    """Scales [n/32, K] of a matrix quantised along its n axis, in the library's word-major
+    layout [n/128, K, 4] (word q of row k holds blocks 4q .. 4q + 3)."""
+    nb, K = st.shape
+    return np.ascontiguousarray(st.reshape(nb // 4, 4, K).transpose(0, 2, 1))
+
+
 def quantized_weights(w1, w2):
     """Oracle MXFP8 of one expert's float32 weights: (w1q, w1s) along d, (w2q, w2s) along I."""
     w1q, w1s = oracle.quantize(np.asarray(w1, np.float64), axis=1)
@@ -139,9 +146,9 @@ def check_expert_forward(v: LayerView, e, w1, w2, st: StageStats, sample=None):
         q1t, s1t = oracle.requantize(w1q, w1s, from_axis=1, to_axis=0)   # [2I, d] blocks along 2I
         q2t, s2t = oracle.requantize(w2q, w2s, from_axis=1, to_axis=0)   # [d, I] blocks along d
         assert np.array_equal(to_np(layer.saved_tensor("w1t")[e]), q1t.T), f"W1t codes of expert {e}"
-        assert np.array_equal(to_np(layer.saved_tensor("w1ts")[e]), s1t.T), f"W1t scales of expert {e}"
+        assert np.array_equal(to_np(layer.saved_tensor("w1ts")[e]), word_major(s1t)), f"W1t scales of expert {e}"
         assert np.array_equal(to_np(layer.saved_tensor("w2t")[e]), q2t.T), f"W2t codes of expert {e}"
-        assert np.array_equal(to_np(layer.saved_tensor("w2ts")[e]), s2t.T), f"W2t scales of expert {e}"
+        assert np.array_equal(to_np(layer.saved_tensor("w2ts")[e]), word_major(s2t)), f"W2t scales of expert {e}"
     r = np.arange(lo, hi) if sample is None else np.asarray(sample)
     rl = r - lo
     G = to_np(layer.saved_tensor("g")[r]).astype(np.float64)
