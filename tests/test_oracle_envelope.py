@@ -107,3 +107,19 @@ def test_envelope_is_zero_without_uncertainty():
     ambiguous = sum(int(np.count_nonzero(v)) for v in env.dH.values())
     assert ambiguous <= total * 1e-3 + 2
     assert F < 1e-5
+
+
+def test_accumulation_model_is_one_value_everywhere():
+    """The envelope's default accumulation model is the one the GPU checks use (the GPU tests
+    measure the gate/up error against it on every run: up to 2^-15.96 * sum|a b| at K = 256)."""
+    import ast
+    import os
+    import stages
+    from oracle import envelope
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    assert envelope.EPS_ACC == stages.EPS == 2.0 ** -15
+    for name in ("tests/test_gpu_layer.py", "tests/test_gpu_dsv3.py", "tests/test_gpu_workloads.py"):
+        tree = ast.parse(open(os.path.join(root, name)).read())
+        eps = [n.value for n in tree.body if isinstance(n, ast.Assign) and
+               any(isinstance(t, ast.Name) and t.id == "EPS" for t in n.targets)]
+        assert len(eps) == 1 and eval(compile(ast.Expression(eps[0]), name, "eval")) == envelope.EPS_ACC, name

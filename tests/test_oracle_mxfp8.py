@@ -159,3 +159,31 @@ def test_requantize_other_axis():
     q3, s3 = oracle.quantize(exact, axis=0)
     assert np.array_equal(q2, q3) and np.array_equal(s2, s3)
     assert mxfp8.BLOCK == 32
+
+
+def test_quantize_range_is_attained():
+    """Tightness of the admissible range: with a few uncertain values in a block, every bound
+    quantize_range reports is the result of some perturbation within the error (brute force over
+    the 3^m corner perturbations), and every corner result lies inside the bounds."""
+    import itertools
+    rng = np.random.default_rng(11)
+    for trial in range(40):
+        a = (rng.standard_normal(32) * 2.0 ** rng.integers(-3, 4)).astype(np.float32).astype(np.float64)
+        unc = rng.choice(32, size=3, replace=False)
+        if trial % 2:
+            unc[0] = int(np.argmax(np.abs(a)))       # the block maximum itself uncertain
+        err = np.zeros(32)
+        err[unc] = np.abs(a[unc]) * 2.0 ** -rng.integers(3, 7, size=3)
+        nom, lo, hi = oracle.quantize_range(a[None], err[None], axis=1)
+        results = []
+        for signs in itertools.product((-1.0, 0.0, 1.0), repeat=3):
+            b = a.copy()
+            b[unc] += np.array(signs) * err[unc]
+            q, s = oracle.quantize(b[None], axis=1)
+            results.append(oracle.dequantize(q, s, axis=1)[0])
+        results = np.array(results)
+        assert np.all(results >= lo[0]) and np.all(results <= hi[0])
+        # attained: for the uncertain values and every value whose bound moved
+        moved = np.where((lo[0] != nom[0]) | (hi[0] != nom[0]))[0]
+        for i in set(moved.tolist()) | set(unc.tolist()):
+            assert results[:, i].min() == lo[0, i] and results[:, i].max() == hi[0, i], (trial, i)
