@@ -138,10 +138,11 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ L, int T
 
 // ----------------------------------------------------------------------------- schedule
 //
-// Expert-major stable permutation of the T*k routed slots in three passes: per 64-token block
-// counts, a per-expert exclusive scan over blocks plus the expert offsets, and a scatter in which
-// one thread per expert walks its block's tokens in order.  Shared experts own the rows after
-// the routed ones (all T tokens, in order).
+// Expert-major stable permutation of the T*k routed slots in four passes: per 64-token block
+// counts; a wavefront scan of each expert's counts over the blocks (one wave per expert); a
+// workgroup scan of the per-expert totals into the offset tables; and a scatter in which one
+// thread per expert walks its block's tokens in order.  Shared experts own the rows after the
+// routed ones (all T tokens, in order).
 
 constexpr int kBlkTok = kSchedBlockTokens;
 
@@ -156,41 +157,71 @@ __global__ __launch_bounds__(256) void k_sched_hist(SchedBuild p) {
   for (int e = threadIdx.x; e < p.E; e += blockDim.x) p.blkcnt[(size_t)blockIdx.x * p.E + e] = cnt[e];
 }
 
-__global__ __launch_bounds__(1024) void k_sched_scan(SchedBuild p, int nblk) {
-  const int n_exp = p.E + p.S;
-  for (int e = threadIdx.x; e < p.E; e += blockDim.x) {
-    int run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      int c = p.blkcnt[(size_t)b * p.E + e];
-      p.blkcnt[(size_t)b * p.E + e] = run;
-      run += c;
-    }
-    p.counts[e] = run;
+// Inclusive prefix sum over the 64 lanes of a wave (wavefront scan: log2(64) shifted adds).
+template <class T>
+MOE_DEV T wave_incl_scan(T v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const T u = __shfl_up(v, o);
+    if (l >= o) v += u;
   }
-  for (int e = p.E + threadIdx.x; e < n_exp; e += blockDim.x) p.counts[e] = p.T;
+  return v;
+}
+
+// One wave per expert: the expert's per-block counts (a column of blkcnt) are replaced by their
+// exclusive prefix over blocks, 64 blocks per wavefront scan, and the total is the expert's
+// row count.
+__global__ __launch_bounds__(64) void k_sched_colscan(SchedBuild p, int nblk) {
+  const int e = blockIdx.x, l = lane_id();
+  int run = 0;
+  for (int b0 = 0; b0 < nblk; b0 += 64) {
+    const int b = b0 + l;
+    const int c = b < nblk ? p.blkcnt[(size_t)b * p.E + e] : 0;
+    const int incl = wave_incl_scan(c);
+    if (b < nblk) p.blkcnt[(size_t)b * p.E + e] = run + incl - c;
+    run += __shfl(incl, 63);
+  }
+  if (l == 0) p.counts[e] = run;
+}
+
+// One workgroup: exclusive prefixes over the experts (routed, then shared with T rows each) of
+// the counts, the counts rounded up to 32 and to 128, the 256-row tiles and the 64-token tiles,
+// by wavefront scans within waves and one scan of the wave totals.
+__global__ __launch_bounds__(1024) void k_sched_offsets(SchedBuild p) {
+  __shared__ int64_t wsum[16][5];
+  const int n_exp = p.E + p.S;
+  const int i = threadIdx.x, l = lane_id(), w = i >> 6;
+  int c = 0;
+  if (i < p.E) c = p.counts[i];
+  else if (i < n_exp) c = p.T;
+  int64_t v[5] = {c, (c + 31) / 32 * 32, (c + 127) / 128 * 128, (c + 255) / 256, (c + 127) / 128 * 2};
+  int64_t incl[5];
+#pragma unroll
+  for (int q = 0; q < 5; ++q) {
+    incl[q] = wave_incl_scan(v[q]);
+    if (l == 63) wsum[w][q] = incl[q];
+  }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int off = 0, poff = 0, tile = 0, t64 = 0;
-    int64_t tok = 0;
-    for (int e = 0; e < n_exp; ++e) {
-      p.offsets[e] = off;
-      p.poffsets[e] = poff;
-      p.tok_off[e] = tok;
-      p.tile_start[e] = tile;
-      p.tile64[e] = t64;
-      int c = p.counts[e];
-      off += c;
-      poff += (c + 31) / 32 * 32;
-      int c128 = (c + 127) / 128 * 128;
-      tok += c128;
-      tile += (c + 255) / 256;
-      t64 += c128 / 64;
+  if (w == 0) {  // exclusive scan of the 16 wave totals, by lanes 0 .. 15
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+      const int64_t t = l < 16 ? wsum[l][q] : 0;
+      const int64_t in = wave_incl_scan(t);
+      if (l < 16) wsum[l][q] = in - t;
     }
-    p.offsets[n_exp] = off;
-    p.poffsets[n_exp] = poff;
-    p.tok_off[n_exp] = tok;
-    p.tile_start[n_exp] = tile;
-    p.tile64[n_exp] = t64;
+  }
+  __syncthreads();
+  int64_t ex[5];
+#pragma unroll
+  for (int q = 0; q < 5; ++q) ex[q] = wsum[w][q] + incl[q] - v[q];
+  if (i >= p.E && i < n_exp) p.counts[i] = c;
+  if (i <= n_exp) {  // thread n_exp writes the totals (its own values are zero)
+    p.offsets[i] = (int32_t)ex[0];
+    p.poffsets[i] = (int32_t)ex[1];
+    p.tok_off[i] = ex[2];
+    p.tile_start[i] = (int32_t)ex[3];
+    p.tile64[i] = (int32_t)ex[4];
   }
 }
 
@@ -233,7 +264,8 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int score, int3
 hipError_t launch_schedule(const SchedBuild& p, hipStream_t st) {
   const int nblk = (p.T + kBlkTok - 1) / kBlkTok;
   hipLaunchKernelGGL(k_sched_hist, dim3(nblk), dim3(256), p.E * sizeof(int32_t), st, p);
-  hipLaunchKernelGGL(k_sched_scan, dim3(1), dim3(1024), 0, st, p, nblk);
+  hipLaunchKernelGGL(k_sched_colscan, dim3(p.E), dim3(64), 0, st, p, nblk);
+  hipLaunchKernelGGL(k_sched_offsets, dim3(1), dim3(1024), 0, st, p);
   hipLaunchKernelGGL(k_sched_scatter, dim3(nblk), dim3(256), kBlkTok * p.k * sizeof(int32_t), st, p);
   return hipGetLastError();
 }
