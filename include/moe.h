@@ -217,6 +217,20 @@ moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, c
                    float* y_f32, void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
                    hipStream_t stream);
 
+/* moe_fwd without a workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).  Same arguments and
+ * results as moe_fwd (bit for bit); the forward's scratch (the device status word and the
+ * schedule's per-block expert counts, 256 + 4 * ceil(T / 64) * E bytes) lives in a static device
+ * array of MOE_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on until the
+ * process ends.  Returns MOE_EWORKSPACE when the configuration needs more scratch than that,
+ * MOE_EINVAL with MOE_F_RING_DISPATCH.  Nothing is allocated or freed.  Every call on one GPU
+ * shares that GPU's scratch: calls that overlap on one GPU (different streams, threads) race and
+ * must be ordered by the caller.  The status word is not readable through moe_device_status. */
+#define MOE_NOALLOC_SCRATCH_BYTES (4u << 20)
+moe_status moe_fwd_noalloc(const moe_config* cfg, const void* x, const void* w_router, const float* router_bias,
+                           const uint8_t* w1q, const uint8_t* w1s, const uint8_t* w2q, const uint8_t* w2s,
+                           void* y_bf16, float* y_f32, void* saved, size_t saved_bytes, hipStream_t stream);
+
 /* Backward pass for upstream gradient dy [T, d] bf16, reusing `saved` from moe_fwd of the same
  * inputs and configuration (knowledge card, 方法/产品要点: pull-based reverse-combine, push-based
  * reverse-dispatch, schedule reused; article "Cursor 為 Composer 改造 MoE 訓練…", section

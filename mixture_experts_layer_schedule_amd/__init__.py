@@ -23,8 +23,9 @@ MOE_F_FORWARD_ONLY = 16
 MOE_DEV_RING_TIMEOUT, MOE_DEV_NONFINITE_LOGIT = 1, 2
 
 # every symbol include/moe.h declares
-EXPORTS = ("moe_query", "moe_quantize_mxfp8", "moe_requant_transpose", "moe_fwd", "moe_bwd",
+EXPORTS = ("moe_query", "moe_quantize_mxfp8", "moe_requant_transpose", "moe_fwd", "moe_fwd_noalloc", "moe_bwd",
            "moe_set_phase_events", "moe_device_status", "moe_strerror")
+MOE_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 # phases of moe_fwd / moe_bwd (include/moe.h, MOE_PH_*)
 PHASES = ("fwd_begin", "quant_x", "router", "topk", "schedule", "gateup", "down", "combine",
@@ -74,6 +75,7 @@ def lib() -> ctypes.CDLL:
         L.moe_quantize_mxfp8.argtypes = [P, ctypes.c_int, I64, I64, P, P, P]
         L.moe_requant_transpose.argtypes = [P, P, I64, I64, I64, P, P, P]
         L.moe_fwd.argtypes = [ctypes.POINTER(moe_config), P, P, P, P, P, P, P, P, P, P, SZ, P, SZ, P]
+        L.moe_fwd_noalloc.argtypes = [ctypes.POINTER(moe_config), P, P, P, P, P, P, P, P, P, P, SZ, P]
         L.moe_bwd.argtypes = [ctypes.POINTER(moe_config), P, P, P, P, SZ, P, P, P, P, P, P, SZ, P]
         L.moe_set_phase_events.argtypes = [P, I32]
         L.moe_device_status.argtypes = [P, ctypes.POINTER(I32)]
@@ -149,6 +151,13 @@ def moe_fwd(cfg, x, w_router, router_bias, w1q, w1s, w2q, w2s, y_bf16, y_f32, sa
     _check(lib().moe_fwd(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w1q), _ptr(w1s),
                          _ptr(w2q), _ptr(w2s), _ptr(y_bf16), _ptr(y_f32), _ptr(saved), _nbytes(saved, saved_bytes),
                          _ptr(workspace), _nbytes(workspace, workspace_bytes), _stream(stream)), "moe_fwd")
+
+
+def moe_fwd_noalloc(cfg, x, w_router, router_bias, w1q, w1s, w2q, w2s, y_bf16, y_f32, saved, stream=None,
+                    saved_bytes=None) -> None:
+    _check(lib().moe_fwd_noalloc(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w1q),
+                                 _ptr(w1s), _ptr(w2q), _ptr(w2s), _ptr(y_bf16), _ptr(y_f32), _ptr(saved),
+                                 _nbytes(saved, saved_bytes), _stream(stream)), "moe_fwd_noalloc")
 
 
 def moe_bwd(cfg, dy, x, w_router, saved, dx_bf16, dx_f32, dw_router, dw1, dw2, workspace, stream=None,

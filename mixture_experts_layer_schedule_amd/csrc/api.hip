@@ -205,54 +205,44 @@ SchedView sched_view(const void* saved, const moe_saved_layout& sl, const Dims& 
   return v;
 }
 
-}  // namespace
+// Static scratch of moe_fwd_noalloc: the status word and the schedule's per-block expert counts,
+// in a file-scope device array (each GPU the library runs on holds its own copy until the
+// process ends).  Host code never uses the array's name as an address: the address of each
+// device's copy comes from hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
-extern "C" {
+size_t noalloc_scratch_bytes(const Dims& m) { return kAlign + (size_t)4 * m.nblk * m.E; }
 
-moe_status moe_query(const moe_config* cfg, size_t* workspace_bytes, moe_saved_layout* saved,
-                     moe_workspace_layout* work) {
-  moe_status st = check_config(cfg);
-  if (st != MOE_OK) return st;
-  Dims m = dims(*cfg);
-  const moe_workspace_layout wl = work_layout(m);
-  if (workspace_bytes) *workspace_bytes = wl.total;
-  if (saved) *saved = saved_layout(m, cfg->flags);
-  if (work) *work = wl;
+uint8_t* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+moe_status device_scratch(uint8_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ELAUNCH;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_ELAUNCH;
+    g_scratch_ptr[dev] = (uint8_t*)ptr;
+  }
+  *out = g_scratch_ptr[dev];
   return MOE_OK;
 }
 
-moe_status moe_quantize_mxfp8(const void* src, int src_is_f32, int64_t rows, int64_t cols, uint8_t* q,
-                              uint8_t* scales, hipStream_t stream) {
-  if (!src || !q || !scales) return MOE_EINVAL;
-  if (rows < 0 || cols < 0 || cols % 32) return MOE_ESHAPE;
-  if (!aligned(src, 16) || !aligned(q, 16)) return MOE_EALIGN;
-  return launch_quant_rows(src, src_is_f32 ? 1 : 0, rows, cols, q, scales, stream) == hipSuccess ? MOE_OK
-                                                                                                : MOE_ELAUNCH;
-}
+// The forward pass over the caller's buffers and a scratch descriptor (the workspace's, or the
+// library's static scratch for moe_fwd_noalloc).
+struct FwdScratch {
+  int32_t* status;      // device status word
+  int32_t* blkcnt;      // [ceil(T/64), E] per-block expert counts
+  uint8_t *ring, *ring_s;
+  int32_t* ring_flags;
+};
 
-moe_status moe_requant_transpose(const uint8_t* q, const uint8_t* scales, int64_t batch, int64_t rows, int64_t cols,
-                                 uint8_t* qt, uint8_t* st, hipStream_t stream) {
-  if (!q || !scales || !qt || !st) return MOE_EINVAL;
-  if (batch < 0 || rows < 0 || cols < 0 || rows % 64 || cols % 64) return MOE_ESHAPE;
-  if (!aligned(q, 16) || !aligned(qt, 16)) return MOE_EALIGN;
-  return launch_requant_t(q, scales, batch, rows, cols, qt, st, stream) == hipSuccess ? MOE_OK : MOE_ELAUNCH;
-}
-
-moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, const float* router_bias,
-                   const uint8_t* w1q, const uint8_t* w1s, const uint8_t* w2q, const uint8_t* w2s, void* y_bf16,
-                   float* y_f32, void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
-                   hipStream_t stream) {
-  moe_status st = check_config(cfg);
-  if (st != MOE_OK) return st;
-  if (!x || !w_router || !w1q || !w1s || !w2q || !w2s || !y_bf16 || !saved || !workspace) return MOE_EINVAL;
-  if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(w1q, 16) || !aligned(w2q, 16) || !aligned(y_bf16, 16) ||
-      (y_f32 && !aligned(y_f32, 16)) || !aligned(saved, kAlign) || !aligned(workspace, kAlign))
-    return MOE_EALIGN;
-  const Dims m = dims(*cfg);
-  const moe_saved_layout sl = saved_layout(m, cfg->flags);
-  const moe_workspace_layout wl = work_layout(m);
-  if (saved_bytes < sl.total || workspace_bytes < wl.total) return MOE_EWORKSPACE;
-  if ((st = ensure_init()) != MOE_OK) return st;
+moe_status forward_impl(const moe_config* cfg, const Dims& m, const moe_saved_layout& sl, const void* x,
+                        const void* w_router, const float* router_bias, const uint8_t* w1q, const uint8_t* w1s,
+                        const uint8_t* w2q, const uint8_t* w2s, void* y_bf16, float* y_f32, void* saved,
+                        const FwdScratch& sc, hipStream_t stream) {
   const int d = (int)m.d, I = (int)m.I;
   const bool want_wt = !(cfg->flags & MOE_F_FORWARD_ONLY);
 
@@ -261,7 +251,7 @@ moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, c
   float* logits = at<float>(saved, sl.logits);
   int32_t* idx = at<int32_t>(saved, sl.idx);
   float* w = at<float>(saved, sl.w);
-  int32_t* status = at<int32_t>(workspace, wl.status);
+  int32_t* status = sc.status;
 
   mark(stream, MOE_PH_FWD_BEGIN);
   MOE_TRY(launch_quant_rows(x, 0, m.T, m.d, xq, xs, stream));
@@ -273,7 +263,7 @@ moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, c
 
   SchedBuild sb;
   sb.idx = idx;
-  sb.blkcnt = at<int32_t>(workspace, wl.blkcnt);
+  sb.blkcnt = sc.blkcnt;
   sb.counts = at<int32_t>(saved, sl.counts);
   sb.offsets = at<int32_t>(saved, sl.offsets);
   sb.poffsets = at<int32_t>(saved, sl.poffsets);
@@ -329,9 +319,9 @@ moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, c
     ra.u = ga.u;
     ra.hq = ga.hq;
     ra.hs = ga.hs;
-    ra.ring = at<uint8_t>(workspace, wl.ring);
-    ra.ring_s = at<uint8_t>(workspace, wl.ring_s);
-    ra.flags = at<int32_t>(workspace, wl.ring_flags);
+    ra.ring = sc.ring;
+    ra.ring_s = sc.ring_s;
+    ra.flags = sc.ring_flags;
     ra.n_flags = (int)(2 * m.nslots + 1);
     ra.ready = ra.flags;
     ra.done = ra.flags + m.nslots;
@@ -363,6 +353,89 @@ moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, c
   MOE_TRY(launch_combine(da.yslot, w, (int)m.T, (int)m.k, (int)m.S, d, (uint16_t*)y_bf16, y_f32, stream));
   mark(stream, MOE_PH_COMBINE);
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_query(const moe_config* cfg, size_t* workspace_bytes, moe_saved_layout* saved,
+                     moe_workspace_layout* work) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  Dims m = dims(*cfg);
+  const moe_workspace_layout wl = work_layout(m);
+  if (workspace_bytes) *workspace_bytes = wl.total;
+  if (saved) *saved = saved_layout(m, cfg->flags);
+  if (work) *work = wl;
+  return MOE_OK;
+}
+
+moe_status moe_quantize_mxfp8(const void* src, int src_is_f32, int64_t rows, int64_t cols, uint8_t* q,
+                              uint8_t* scales, hipStream_t stream) {
+  if (!src || !q || !scales) return MOE_EINVAL;
+  if (rows < 0 || cols < 0 || cols % 32) return MOE_ESHAPE;
+  if (!aligned(src, 16) || !aligned(q, 16)) return MOE_EALIGN;
+  return launch_quant_rows(src, src_is_f32 ? 1 : 0, rows, cols, q, scales, stream) == hipSuccess ? MOE_OK
+                                                                                                : MOE_ELAUNCH;
+}
+
+moe_status moe_requant_transpose(const uint8_t* q, const uint8_t* scales, int64_t batch, int64_t rows, int64_t cols,
+                                 uint8_t* qt, uint8_t* st, hipStream_t stream) {
+  if (!q || !scales || !qt || !st) return MOE_EINVAL;
+  if (batch < 0 || rows < 0 || cols < 0 || rows % 64 || cols % 64) return MOE_ESHAPE;
+  if (!aligned(q, 16) || !aligned(qt, 16)) return MOE_EALIGN;
+  return launch_requant_t(q, scales, batch, rows, cols, qt, st, stream) == hipSuccess ? MOE_OK : MOE_ELAUNCH;
+}
+
+moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, const float* router_bias,
+                   const uint8_t* w1q, const uint8_t* w1s, const uint8_t* w2q, const uint8_t* w2s, void* y_bf16,
+                   float* y_f32, void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!x || !w_router || !w1q || !w1s || !w2q || !w2s || !y_bf16 || !saved || !workspace) return MOE_EINVAL;
+  if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(w1q, 16) || !aligned(w2q, 16) || !aligned(y_bf16, 16) ||
+      (y_f32 && !aligned(y_f32, 16)) || !aligned(saved, kAlign) || !aligned(workspace, kAlign))
+    return MOE_EALIGN;
+  const Dims m = dims(*cfg);
+  const moe_saved_layout sl = saved_layout(m, cfg->flags);
+  const moe_workspace_layout wl = work_layout(m);
+  if (saved_bytes < sl.total || workspace_bytes < wl.total) return MOE_EWORKSPACE;
+  if ((st = ensure_init()) != MOE_OK) return st;
+  FwdScratch sc;
+  sc.status = at<int32_t>(workspace, wl.status);
+  sc.blkcnt = at<int32_t>(workspace, wl.blkcnt);
+  sc.ring = at<uint8_t>(workspace, wl.ring);
+  sc.ring_s = at<uint8_t>(workspace, wl.ring_s);
+  sc.ring_flags = at<int32_t>(workspace, wl.ring_flags);
+  return forward_impl(cfg, m, sl, x, w_router, router_bias, w1q, w1s, w2q, w2s, y_bf16, y_f32, saved, sc, stream);
+}
+
+moe_status moe_fwd_noalloc(const moe_config* cfg, const void* x, const void* w_router, const float* router_bias,
+                           const uint8_t* w1q, const uint8_t* w1s, const uint8_t* w2q, const uint8_t* w2s,
+                           void* y_bf16, float* y_f32, void* saved, size_t saved_bytes, hipStream_t stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->flags & MOE_F_RING_DISPATCH) return MOE_EINVAL;  // the ring buffer lives in a workspace
+  if (!x || !w_router || !w1q || !w1s || !w2q || !w2s || !y_bf16 || !saved) return MOE_EINVAL;
+  if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(w1q, 16) || !aligned(w2q, 16) || !aligned(y_bf16, 16) ||
+      (y_f32 && !aligned(y_f32, 16)) || !aligned(saved, kAlign))
+    return MOE_EALIGN;
+  const Dims m = dims(*cfg);
+  const moe_saved_layout sl = saved_layout(m, cfg->flags);
+  if (saved_bytes < sl.total) return MOE_EWORKSPACE;
+  if (noalloc_scratch_bytes(m) > kScratchBytes) return MOE_EWORKSPACE;  // beyond the static scratch
+  if ((st = ensure_init()) != MOE_OK) return st;
+  uint8_t* base = nullptr;
+  if ((st = device_scratch(&base)) != MOE_OK) return st;
+  FwdScratch sc;
+  sc.status = (int32_t*)base;
+  sc.blkcnt = (int32_t*)(base + kAlign);
+  sc.ring = nullptr;
+  sc.ring_s = nullptr;
+  sc.ring_flags = nullptr;
+  return forward_impl(cfg, m, sl, x, w_router, router_bias, w1q, w1s, w2q, w2s, y_bf16, y_f32, saved, sc, stream);
 }
 
 moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const void* w_router, const void* saved,
