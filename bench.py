@@ -7,6 +7,7 @@ synthetic inputs (moe_inputs).  A step is moe_fwd + moe_bwd over one batch with 
 already resident in HBM.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+  python bench.py --config dsv3_fwd --forward-only      (a forward workload, moe_fwd alone)
 """
 from __future__ import annotations
 
@@ -24,6 +25,7 @@ sys.path.insert(0, ROOT)
 MXFP8_PEAK = 5.0e15       # dense MXFP8 MFMA, FLOP/s (MI355X published)
 HBM_PEAK = 8.0e12         # HBM3E, B/s (MI355X published)
 METRIC = "MoE layer fwd+bwd TFLOPS & tokens/s at DSV3 shape; % of MXFP8 MFMA peak"
+METRIC_FWD = "MoE layer forward TFLOPS & tokens/s; % of MXFP8 MFMA peak"
 
 
 def log(*a):
@@ -36,21 +38,24 @@ def log(*a):
 # and once out per stage, dW once, the dense E-times work not counted.  R = T*k routed rows,
 # NX experts; weights are MXFP8 (1 byte + 1/32 scale byte per value); activations as stored.
 
-def phase_work(cfg, tok_pad: int) -> dict:
+def phase_work(cfg, tok_pad: int, backward: bool = True) -> dict:
+    """With ``backward`` the forward GEMMs also write the weights requantised along the other axis
+    (W1^T, W2^T: the dgrad GEMMs' operands), once per weight byte."""
     T, d, E, k, I, S = cfg.T, cfg.d, cfg.E, cfg.k, cfg.inter, cfg.n_shared
     NX, R = E + S, T * cfg.k + S * T
     q = 1 + 1 / 32  # MXFP8 bytes per value
     w1 = NX * 2 * I * d * q
     w2 = NX * d * I * q
+    wt = 1.0 if backward else 0.0
     return {
         "quant_x": (0.0, T * d * 2 + T * d * q),
         "router": (2.0 * T * d * E, T * d * 2 + E * d * 2 + T * E * 4),
-        "gateup": (2.0 * R * d * 2 * I, w1 + R * d * q + R * I * (4 + 4 + q)),
-        "down": (2.0 * R * I * d, w2 + R * I * q + R * d * 4),
+        "gateup": (2.0 * R * d * 2 * I, w1 * (1 + wt) + R * d * q + R * I * (4 + 4 + q)),
+        "down": (2.0 * R * I * d, w2 * (1 + wt) + R * I * q + R * d * 4),
         "combine": (0.0, R * d * 4 + T * d * (2 + 4)),
         "quant_dy": (0.0, T * d * 2 + T * d * q),
         "router_bwd": (2.0 * T * k * d, T * k * d * 4 + T * d * 2),
-        "requant_w": (0.0, 0.0),  # done inside the dgrad GEMMs (their bytes count the weights once)
+        "requant_w": (0.0, 0.0),  # done inside the forward GEMMs (counted there)
         "dgrad_down": (2.0 * R * d * I, w2 + R * d * q + R * I * 8 + R * 2 * I * q),
         "dgrad_gateup": (2.0 * R * 2 * I * d, w1 + R * 2 * I * q + R * d * 4),
         "dx_reduce": (0.0, R * d * 4 + T * d * 6),
@@ -134,9 +139,24 @@ def measured_traffic(phase: str, ring: bool):
 
 # ----------------------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(cfg, inp, n_experts: int) -> dict:
+def host_resources() -> dict:
+    """Cores this process may run on, the BLAS pool's thread count and the host's RAM."""
+    affinity = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] + [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    try:
+        ram_gb = os.sysconf("SC_PAGE_SIZE") * os.sysconf("SC_PHYS_PAGES") / 2 ** 30
+    except (ValueError, OSError):  # pragma: no cover
+        ram_gb = float("nan")
+    return {"affinity_cores": affinity, "blas_threads": blas, "ram_gib": round(ram_gb, 1)}
+
+
+def cpu_baseline(cfg, inp, n_experts: int, backward: bool = True) -> dict:
     """The float64 oracle timed on a bounded sample: full router/top-k/schedule/combine work on all
-    tokens, the expert forward+backward (with the transposed weight requantisation) on
+    tokens, the expert forward (+ backward with the transposed weight requantisation) on
     ``n_experts`` experts, scaled to the whole layer."""
     import numpy as np
 
@@ -144,11 +164,9 @@ def cpu_baseline(cfg, inp, n_experts: int) -> dict:
     import oracle
     from oracle.layer import _qdq
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+    res = host_resources()
+    # the oracle's float64 matrix products run on the BLAS pool, everything else on one thread
+    cores = max(1, min(res["affinity_cores"], res["blas_threads"]))
     x = inp.x.astype(np.float64)
     t0 = time.perf_counter()
     L = oracle.router_logits(x, inp.w_r, inp.bias)
@@ -157,8 +175,9 @@ def cpu_baseline(cfg, inp, n_experts: int) -> dict:
     sched = oracle.build_schedule(idx, cfg.E)
     xq, xs = oracle.quantize(x, axis=1)
     X = oracle.dequantize(xq, xs, axis=1)
-    dyq, dys = oracle.quantize(inp.dy.astype(np.float64), axis=1)
-    DY = oracle.dequantize(dyq, dys, axis=1)
+    if backward:
+        dyq, dys = oracle.quantize(inp.dy.astype(np.float64), axis=1)
+        DY = oracle.dequantize(dyq, dys, axis=1)
     t_dense = time.perf_counter() - t0
     # expert sample: experts with the median load
     order = np.argsort(sched.counts)
@@ -173,19 +192,22 @@ def cpu_baseline(cfg, inp, n_experts: int) -> dict:
         wrow = w.reshape(-1)[sched.perm[sched.offsets[e]:sched.offsets[e + 1]]]
         t1 = time.perf_counter()
         fw = oracle.expert_forward(X[toks], W1, W2)
-        W2t = _qdq(W2, 0, True)[2]
-        W1t = _qdq(W1, 0, True)[2]
-        oracle.expert_backward(fw, X[toks], DY[toks], wrow, W1t, W2t)
+        if backward:
+            W2t = _qdq(W2, 0, True)[2]
+            W1t = _qdq(W1, 0, True)[2]
+            oracle.expert_backward(fw, X[toks], DY[toks], wrow, W1t, W2t)
         t_exp += time.perf_counter() - t1
         rows += len(toks)
     # combine-side work on the sample's rows, scaled like the experts
     t_total = t_dense + t_exp * (cfg.T * cfg.k) / max(rows, 1)
+    what = "forward/backward incl. weight requantisation" if backward else "forward"
     return {
         "value": cfg.T / t_total, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-        "sample": (f"float64 NumPy oracle: router, top-k, schedule and x/dy quantisation on all {cfg.T} tokens "
-                   f"({t_dense:.1f} s) + expert forward/backward incl. weight requantisation on {len(sample)} "
+        "sample": (f"float64 NumPy oracle: router, top-k, schedule and activation quantisation on all {cfg.T} "
+                   f"tokens ({t_dense:.1f} s) + expert {what} on {len(sample)} "
                    f"median-load experts ({rows} rows, {t_exp:.1f} s), scaled by routed rows "
                    f"{cfg.T * cfg.k}/{rows}; estimated layer time {t_total:.1f} s"),
+        **res,
     }
 
 
@@ -205,6 +227,8 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (scales HBM byte counters)")
     ap.add_argument("--flags", type=int, default=0, help="moe_config.flags (2 = ring dispatch)")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="time moe_fwd alone (MOE_F_FORWARD_ONLY: no state saved for a backward pass)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one MI355X: the layer runs with every expert resident on a single GPU; "
@@ -218,15 +242,15 @@ def main() -> int:
     import mixture_experts_layer_schedule_amd as moe
     from mixture_experts_layer_schedule_amd import MoeLayer
 
-    cfg = moe_inputs.CONFIGS[args.config]
-    if not cfg.backward:
-        cfg = cfg.with_(backward=True)
+    fwd_only = args.forward_only
+    cfg = moe_inputs.CONFIGS[args.config].with_(backward=not fwd_only)
     if args.tokens:
         cfg = cfg.with_(T=args.tokens, name=f"{cfg.name}_T{args.tokens}")
+    flags = args.flags | (moe.MOE_F_FORWARD_ONLY if fwd_only else 0)
     t0 = time.time()
-    inp = moe_inputs.layer_inputs(cfg, with_dy=True)
-    layer = MoeLayer.from_config(cfg, with_backward=True, flags=args.flags)
-    layer.set_inputs(inp.x_bits, inp.w_r_bits, inp.bias, inp.dy_bits)
+    inp = moe_inputs.layer_inputs(cfg, with_dy=not fwd_only)
+    layer = MoeLayer.from_config(cfg, with_backward=not fwd_only, flags=flags)
+    layer.set_inputs(inp.x_bits, inp.w_r_bits, inp.bias, None if fwd_only else inp.dy_bits)
     log(f"[bench] inputs on device; drawing and quantising {cfg.E + cfg.n_shared} experts")
     layer.load_experts(moe_inputs.iter_expert_weights(cfg, threads=min(16, os.cpu_count() or 8)))
     log(f"[bench] setup {time.time() - t0:.1f} s")
@@ -245,7 +269,8 @@ def main() -> int:
 
     def step():
         layer.forward(stream)
-        layer.backward(stream)
+        if not fwd_only:
+            layer.backward(stream)
 
     for i in range(args.warmup):
         step()
@@ -265,6 +290,8 @@ def main() -> int:
             total += start.elapsed_time(stop)
             prev = None
             for p, name in enumerate(moe.PHASES):
+                if name == "bwd_begin" and fwd_only:
+                    break
                 if name in ("fwd_begin", "bwd_begin"):
                     prev = p
                     continue
@@ -275,26 +302,29 @@ def main() -> int:
     # the timed region: the library's default schedule (backward branch on a second stream)
     ms, phase_ms_timed = timed(args.steps)
     log(f"[bench] {args.steps} steps, {ms:.3f} ms/step")
-    # per-phase breakdown: the same step with every kernel in launch order on one stream
-    layer.cfg.flags |= moe.MOE_F_SERIAL_BWD
-    n_serial = min(args.steps, 3)
-    ms_serial, phase_ms = timed(n_serial)
-    layer.cfg.flags &= ~moe.MOE_F_SERIAL_BWD
+    if fwd_only:  # the forward runs on one stream: its phase marks come from the timed region
+        ms_serial, phase_ms = ms, phase_ms_timed
+    else:
+        # per-phase breakdown: the same step with every kernel in launch order on one stream
+        layer.cfg.flags |= moe.MOE_F_SERIAL_BWD
+        n_serial = min(args.steps, 3)
+        ms_serial, phase_ms = timed(n_serial)
+        layer.cfg.flags &= ~moe.MOE_F_SERIAL_BWD
+        log(f"[bench] {n_serial} steps in launch order (phase breakdown), {ms_serial:.3f} ms/step")
     torch.cuda.synchronize()
     moe.moe_set_phase_events(None, 0)
-    log(f"[bench] {n_serial} steps in launch order (phase breakdown), {ms_serial:.3f} ms/step")
     code = moe.moe_device_status(layer.workspace)
     if code != 0:
         log(f"[bench] device status {code}")
         return 1
 
     tok_off = layer.saved_tensor("tok_off").cpu().numpy()
-    work = phase_work(cfg, int(tok_off[-1]))
+    work = phase_work(cfg, int(tok_off[-1]), backward=not fwd_only)
+    gemms = ("gateup", "down") if fwd_only else ("gateup", "down", "dgrad_down", "dgrad_gateup", "wgrad_down",
+                                                 "wgrad_gateup")
     flops_fwd = sum(work[p][0] for p in ("gateup", "down"))
-    flops_gemm = sum(work[p][0] for p in ("gateup", "down", "dgrad_down", "dgrad_gateup", "wgrad_down",
-                                          "wgrad_gateup"))
-    gemm_ms = sum(phase_ms[p] for p in ("gateup", "down", "dgrad_down", "dgrad_gateup", "wgrad_down",
-                                         "wgrad_gateup"))
+    flops_gemm = sum(work[p][0] for p in gemms)
+    gemm_ms = sum(phase_ms[p] for p in gemms)
     tflops = flops_gemm / (ms * 1e-3) / 1e12
     phases = {}
     for p, t in phase_ms.items():
@@ -316,17 +346,19 @@ def main() -> int:
     else:
         roof = {"bound": "hbm", "achieved": round(b / t / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(dom, ring=bool(args.flags & 2))
+    # the committed counters were taken on the default workload only
+    default_run = args.config == "dsv3_fwd_bwd" and not args.tokens and not fwd_only
+    roof["traffic"] = measured_traffic(dom, ring=bool(args.flags & 2)) if default_run else None
     roof["kernel"] = dom
     roof["timed_in"] = "timed region" if clean else "launch-order pass"
 
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU baseline: oracle on a sample of {args.cpu_experts} experts")
-        cpu = cpu_baseline(cfg, inp, args.cpu_experts)
+        cpu = cpu_baseline(cfg, inp, args.cpu_experts, backward=not fwd_only)
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC_FWD if fwd_only else METRIC,
         "value": round(cfg.T / (ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -338,8 +370,9 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "mxfp8",
         "data": "synthetic",
-        "config": {"workload": (f"{cfg.name}: DeepSeek-V3-shape MoE layer fwd+bwd, T={cfg.T} d={cfg.d} "
-                                f"E={cfg.E} k={cfg.k} I={cfg.inter} {cfg.score}, seed {cfg.seed}"),
+        "config": {"workload": (f"{cfg.name}: MoE layer {'fwd' if fwd_only else 'fwd+bwd'}, T={cfg.T} d={cfg.d} "
+                                f"E={cfg.E}{f'+{cfg.n_shared} shared' if cfg.n_shared else ''} k={cfg.k} "
+                                f"I={cfg.inter} {cfg.score}, seed {cfg.seed}"),
                    "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "inter": cfg.inter, "score": cfg.score,
                    "n_shared": cfg.n_shared, "seed": cfg.seed, "parallelism": "single GPU"},
         "tflops": round(tflops, 2),

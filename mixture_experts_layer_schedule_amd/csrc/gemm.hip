@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_down(DgradDownArgs p) {
            w2ts, [&](int r) { return w2ts + (size_t)min(n0 + r, I - 1) * 4; });
     L.bsk = 4 * I;  // word-major scales: stage t's words are plane t
     v16f acc[F][2];
-    mainloop<F, 2>(lds, L, d / KS, acc);
+    mainloop<F, 2, 0, false>(lds, L, d / KS, acc);
     // combine weight of every row of the tile, once, through LDS
     float* wt = (float*)(lds + ((d / KS) % kStages) * STAGE_BYTES);
     if ((int)threadIdx.x < rt.rows) wt[threadIdx.x] = row_weight(s, p.w, rt.r0 + threadIdx.x);
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_gateup(DgradGateUpArgs p)
            w1ts, [&](int r) { return w1ts + (size_t)min(n0 + r, d - 1) * 4; });
     L.bsk = 4 * d;  // word-major scales: stage t's words are plane t
     v16f acc[F][2];
-    mainloop<F, 2>(lds, L, I2 / KS, acc);
+    mainloop<F, 2, 0, false>(lds, L, I2 / KS, acc);
     const int64_t* slot = row_slot_table(s, rt, lds + ((I2 / KS) % kStages) * STAGE_BYTES);
     if (!active) return;
     static_for<F>([&]<int mi>() {
@@ -304,8 +304,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_wgrad(WgradArgs p) {
 // ---------------------------------------------------------------------------------------------
 // launchers
 
-size_t gemm_lds_bytes() { return lds_bytes_for(kStages); }
-static size_t wgrad_lds_bytes() { return lds_bytes_for(2); }
+size_t gemm_lds_bytes() { return GEMM_LDS_BYTES; }
+static size_t wgrad_lds_bytes() { return GEMM_LDS_BYTES; }
 
 hipError_t launch_gemm_gateup(const GateUpArgs& a, int tiles_bound, hipStream_t st) {
   hipLaunchKernelGGL(k_gemm_gateup, dim3(tiles_bound * (a.I / 128)), dim3(512), gemm_lds_bytes(), st, a);

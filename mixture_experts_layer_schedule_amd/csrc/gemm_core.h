@@ -20,10 +20,17 @@
 // direct-to-LDS loads (global_load_lds_dwordx4: no registers in between) while the previous
 // stage is multiplied.  A load instruction moves 8 whole staged rows of 128 bytes, so every
 // request is a full cache line.  Each staged row's eight 16-byte chunks are XOR-swizzled by the
-// row index so that the fragment reads (lane i reads row i) hit distinct banks.  Scales travel
-// the same way, one 4-byte word (4 K blocks) per row and stage.  One barrier per stage: it
-// publishes the stage every wave loaded a share of and retires the buffer that the next loads
-// overwrite.
+// row index so that the fragment reads (lane i reads row i) hit distinct banks.  One barrier per
+// stage: it publishes the stage every wave loaded a share of and retires the buffer that the
+// next loads overwrite.
+//
+// Scales: a stage needs one 4-byte word (4 K blocks) per row, and every operand row's scales
+// lie in a cache line of their own, so loading them stage by stage costs one request per row and
+// stage: as many line requests as the stage's data.  They travel instead in groups of four
+// stages (16 bytes per row, fetched as 4 words by 4 lanes), a quarter of the requests, into two
+// group buffers behind the stage buffers (scale_group below).  Weight scales that are already
+// stored stage-major (the transposed weights of the dgrad GEMMs) keep the per-stage word loads:
+// a stage's words are contiguous there.
 //
 // Each output tile is owned by exactly one workgroup and K is summed in a fixed order, so
 // results are bitwise reproducible.
@@ -45,6 +52,24 @@ constexpr int SCALE_BYTES = (TM + TN) * 4;   // one scale word (4 K blocks) per 
 constexpr int STAGE_BYTES = DATA_BYTES + SCALE_BYTES;
 
 constexpr size_t lds_bytes_for(int nst) { return (size_t)nst * STAGE_BYTES; }
+
+// Scale groups.  Group g holds the words of stages 4g .. 4g + 3 for the tile's A rows (group rows
+// 0 .. 255) and B rows (256 .. 511), 16 bytes per row, in buffer g % 2 behind the two stage
+// buffers.  Group g travels with the data of stage 4g; the buffer's previous group was last read
+// four barriers earlier.  Word c of row r sits at 16 r + 4 (c ^ ((r >> 3) & 3)): 32 consecutive
+// rows reading one word hit 32 distinct banks.
+constexpr int SG_ROW = 16;
+constexpr int SG_BYTES = (TM + TN) * SG_ROW;
+constexpr int SG_BASE = 2 * STAGE_BYTES;
+// byte offsets (from the operand's scale base) of the tile's 512 group rows' scales, written once
+// per tile: the group loads read them from here rather than holding them in registers
+constexpr int SGT_BASE = SG_BASE + 2 * SG_BYTES;
+constexpr size_t GEMM_LDS_BYTES = (size_t)SGT_BASE + (TM + TN) * 4;
+
+MOE_DEV const uint8_t* sg_buf(const uint8_t* lds, int t) { return lds + SG_BASE + ((t >> 2) & 1) * SG_BYTES; }
+MOE_DEV uint8_t* sg_buf(uint8_t* lds, int t) { return lds + SG_BASE + ((t >> 2) & 1) * SG_BYTES; }
+// byte of stage t's word of group row r (r a multiple of 32 plus lane i < 32 in the readers)
+MOE_DEV int sg_pos(int r, int t) { return SG_ROW * r + 4 * ((t & 3) ^ ((r >> 3) & 3)); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -173,28 +198,45 @@ MOE_DEV void lds_load4(const uint8_t* src, uint8_t* dst) {
   __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)dst, 4, 0, AUX);
 }
 
-// A half of the loads of stage t (K range [128t, 128t + 128)) into buffer t % NST: one scale
-// word and F data instructions per wave.  AUX_A: cache-policy bits of the A loads (16 = sc1:
-// device-coherent reads of rows that other workgroups of the same kernel wrote).
-template <int F, int NST, int AUX_A>
-MOE_DEV void issue_a_stage(const TileLoads<F>& L, uint8_t* lds, int t) {
-  const int w = threadIdx.x >> 6;
-  const int k0 = t * KS;
-  uint8_t* st = lds + (t % NST) * STAGE_BYTES;
-  uint8_t* sc = st + DATA_BYTES;
-  lds_load4<AUX_A>(L.asbase + (L.as + ((uint32_t)k0 >> 5)), sc + 256 * w);
-  static_for<F>([&]<int u>() { lds_load16<AUX_A>(L.abase + (L.a[u] + (uint32_t)k0), st + 1024 * (w + 4 * u)); });
+// Scale group of stage t (t % 4 == 0) for 64 group rows [64q, 64q + 64) of one operand: tbl
+// holds the rows' scale offsets from base (the table entry of row 64q); dst = group buffer +
+// 1024 q.  Instruction u fetches rows 64q + 16u .. + 16, lane l word (l % 4) ^ swizzle of row
+// 16u + l / 4 (the lane's LDS word is 4l after 256u); words past the operand's last stage nk - 1
+// repeat that stage's (never read).
+MOE_DEV uint32_t* sg_table(uint8_t* lds) { return (uint32_t*)(lds + SGT_BASE); }
+
+template <int AUX>
+MOE_DEV void scale_group(const uint8_t* base, uint8_t* lds, int q, int dst_off, int t, int nk) {
+  int l = lane_id();
+  // opaque per call: the lane's rows and swizzled words would otherwise be hoisted out of the K
+  // loop and held in registers across the matrix work
+  asm volatile("" : "+v"(l));
+  const uint32_t* tbl = sg_table(lds) + 64 * q;
+  uint8_t* dst = sg_buf(lds, t) + dst_off;
+  static_for<4>([&]<int u>() {
+    const int rl = 16 * u + (l >> 2);
+    const int c = (l & 3) ^ ((rl >> 3) & 3);
+    lds_load4<AUX>(base + (tbl[rl] + 4u * (uint32_t)min(t + c, nk - 1)), dst + 256 * u);
+  });
 }
 
-// Loads of stage t into buffer t % NST: 2 scale words, then F + 8 data instructions per wave.
-template <int F, int NST, int AUX_A>
-MOE_DEV void issue_stage(const TileLoads<F>& L, uint8_t* lds, int t) {
+// Loads of stage t into buffer t % NST: the scale groups every fourth stage, then F + 8 data
+// instructions per wave.  AUX_A: cache-policy bits of the A loads (16 = sc1: device-coherent
+// reads of rows that other workgroups of the same kernel wrote).
+// kGB: B scales in groups (row-major scales); else one word per row and stage, stage t's words
+// at t * L.bsk from the row's (stage-major scales).
+template <int F, int NST, int AUX_A, bool kGB>
+MOE_DEV void issue_stage(const TileLoads<F>& L, uint8_t* lds, int t, int nk) {
   const int w = threadIdx.x >> 6;
   const int k0 = t * KS;
   uint8_t* st = lds + (t % NST) * STAGE_BYTES;
   uint8_t* sc = st + DATA_BYTES;
-  lds_load4<AUX_A>(L.asbase + (L.as + ((uint32_t)k0 >> 5)), sc + 256 * w);
-  lds_load4<0>(L.bsbase + (L.bs + (uint32_t)t * L.bsk), sc + TM * 4 + 256 * w);
+  if ((t & 3) == 0) {
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    scale_group<AUX_A>(L.asbase, lds, wu, 1024 * wu, t, nk);
+    if constexpr (kGB) scale_group<0>(L.bsbase, lds, 4 + wu, TM * SG_ROW + 1024 * wu, t, nk);
+  }
+  if constexpr (!kGB) lds_load4<0>(L.bsbase + (L.bs + (uint32_t)t * L.bsk), sc + TM * 4 + 256 * w);
   static_for<F>([&]<int u>() { lds_load16<AUX_A>(L.abase + (L.a[u] + (uint32_t)k0), st + 1024 * (w + 4 * u)); });
   const uint32_t kb = (uint32_t)t * L.bk;
   static_for<8>([&]<int u>() { lds_load16<0>(L.bbase + (L.b[u] + kb), st + A_STAGE + 1024 * (w + 4 * u)); });
@@ -217,15 +259,20 @@ MOE_DEV void pin_agprs(v16f& a, v16f& b) { asm volatile("" : "+a"(a), "+a"(b)::"
 // read two at a time, one pair ahead of the matrix instructions that use the previous pair
 // (scheduling barriers keep that order): LDS returns in order, so each instruction waits only
 // for its own operands while the next pair is arriving, and few registers hold fragments.
-template <int F>
-MOE_DEV void compute_stage(const uint8_t* st, v16f (&acc)[F][2]) {
+template <int F, bool kGB>
+MOE_DEV void compute_stage(const uint8_t* st, const uint8_t* sg, int t, v16f (&acc)[F][2]) {
   const int l = lane_id(), i = l & 31, h = l >> 5, w = threadIdx.x >> 6;
   const int sw = swz(i);
-  const uint32_t* sc = (const uint32_t*)(st + DATA_BYTES);
   int sa[F], sb[2];
-  static_for<F>([&]<int mi>() { sa[mi] = (int)(sc[32 * mi + i] >> (8 * h)); });
-  sb[0] = (int)(sc[TM + 64 * w + i] >> (8 * h));
-  sb[1] = (int)(sc[TM + 64 * w + 32 + i] >> (8 * h));
+  static_for<F>([&]<int mi>() { sa[mi] = (int)(*(const uint32_t*)(sg + sg_pos(32 * mi + i, t)) >> (8 * h)); });
+  if constexpr (kGB) {
+    sb[0] = (int)(*(const uint32_t*)(sg + sg_pos(TM + 64 * w + i, t)) >> (8 * h));
+    sb[1] = (int)(*(const uint32_t*)(sg + sg_pos(TM + 64 * w + 32 + i, t)) >> (8 * h));
+  } else {
+    const uint32_t* sc = (const uint32_t*)(st + DATA_BYTES);
+    sb[0] = (int)(sc[TM + 64 * w + i] >> (8 * h));
+    sb[1] = (int)(sc[TM + 64 * w + 32 + i] >> (8 * h));
+  }
   constexpr int NG = (F + 1) / 2;
   static_for<2>([&]<int kk>() {
     auto frag = [&](const uint8_t* rp, int s2) {
@@ -263,7 +310,7 @@ MOE_DEV void compute_stage(const uint8_t* st, v16f (&acc)[F][2]) {
 // acc = A_tile * B_tile^T over K = 128 * nk.  Every wave multiplies, also one whose columns lie
 // past N (its B rows are clamped copies and its results are dropped): a branch around the
 // matrix instructions would make the accumulators change register class every iteration.
-template <int F, int NST, int AUX_A = 0>
+template <int F, int NST, int AUX_A = 0, bool kGB = true>
 MOE_DEV void mainloop(uint8_t* lds, const TileLoads<F>& L, int nk, v16f (&acc)[F][2]) {
   static_assert(NST == 2, "two LDS stages");
   static_for<F>([&]<int mi>() {
@@ -271,11 +318,14 @@ MOE_DEV void mainloop(uint8_t* lds, const TileLoads<F>& L, int nk, v16f (&acc)[F
     acc[mi][1] = (v16f){};
   });
   if (nk <= 0) return;
-  issue_stage<F, NST, AUX_A>(L, lds, 0);
+  // this wave's rows' scale offsets (read back by the same wave only: no barrier needed)
+  sg_table(lds)[threadIdx.x] = L.as;
+  if constexpr (kGB) sg_table(lds)[TM + threadIdx.x] = L.bs;
+  issue_stage<F, NST, AUX_A, kGB>(L, lds, 0, nk);
   for (int t = 0; t < nk; ++t) {
     wait_loads_and_sync<0>();  // stage t has landed; every wave is done with stage t - 1
-    if (t + 1 < nk) issue_stage<F, NST, AUX_A>(L, lds, t + 1);
-    compute_stage<F>(lds + (t % NST) * STAGE_BYTES, acc);
+    if (t + 1 < nk) issue_stage<F, NST, AUX_A, kGB>(L, lds, t + 1, nk);
+    compute_stage<F, kGB>(lds + (t % NST) * STAGE_BYTES, sg_buf(lds, t), t, acc);
   }
 }
 
@@ -321,15 +371,15 @@ struct TileLoads8 {
 
 // Loads of stage t into buffer t % 2: one scale word and this wave's share of the data.
 template <int F>
-MOE_DEV void issue_stage8(const TileLoads8<F>& L, uint8_t* lds, int t) {
+MOE_DEV void issue_stage8(const TileLoads8<F>& L, uint8_t* lds, int t, int nk) {
   const int w = threadIdx.x >> 6;
   const uint32_t k0 = (uint32_t)t * KS;
   uint8_t* st = lds + (t % 2) * STAGE_BYTES;
-  uint8_t* scp = st + DATA_BYTES;
-  if (w < 4)
-    lds_load4<0>(L.asbase + (L.sc + (k0 >> 5)), scp + 256 * w);
-  else
-    lds_load4<0>(L.bsbase + (L.sc + (k0 >> 5)), scp + TM * 4 + 256 * (w - 4));
+  // scale group: waves 0-3 the A rows 64w .., waves 4-7 the B rows 64(w - 4) .. (group rows 64w ..)
+  if ((t & 3) == 0) {
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    scale_group<0>(wu < 4 ? L.asbase : L.bsbase, lds, wu, 1024 * wu, t, nk);
+  }
   static_for<TileLoads8<F>::NA>([&]<int u>() {
     const int q = w + 8 * u;
     if (q < 4 * F) lds_load16<0>(L.abase + (L.a[u] + k0), st + 1024 * q);
@@ -340,16 +390,15 @@ MOE_DEV void issue_stage8(const TileLoads8<F>& L, uint8_t* lds, int t) {
 // Multiply one staged K slice (two MFMA steps) for this wave's FH row fragments and two column
 // fragments; A fragments read two at a time ahead of the matrix instructions.
 template <int F>
-MOE_DEV void compute_stage8(const uint8_t* st, v16f (&acc)[(F + 1) / 2][2]) {
+MOE_DEV void compute_stage8(const uint8_t* st, const uint8_t* sg, int t, v16f (&acc)[(F + 1) / 2][2]) {
   constexpr int FH = (F + 1) / 2;
   const int l = lane_id(), i = l & 31, h = l >> 5, w = threadIdx.x >> 6;
   const int wc = w & 3, m0 = (w >> 2) * FH;
   const int sw = swz(i);
-  const uint32_t* sc = (const uint32_t*)(st + DATA_BYTES);
   int sa[FH], sb[2];
-  static_for<FH>([&]<int m>() { sa[m] = (int)(sc[32 * (m0 + m) + i] >> (8 * h)); });
-  sb[0] = (int)(sc[TM + 64 * wc + i] >> (8 * h));
-  sb[1] = (int)(sc[TM + 64 * wc + 32 + i] >> (8 * h));
+  static_for<FH>([&]<int m>() { sa[m] = (int)(*(const uint32_t*)(sg + sg_pos(32 * (m0 + m) + i, t)) >> (8 * h)); });
+  sb[0] = (int)(*(const uint32_t*)(sg + sg_pos(TM + 64 * wc + i, t)) >> (8 * h));
+  sb[1] = (int)(*(const uint32_t*)(sg + sg_pos(TM + 64 * wc + 32 + i, t)) >> (8 * h));
   constexpr int NG = (FH + 1) / 2;
   static_for<2>([&]<int kk>() {
     auto frag = [&](const uint8_t* rp, int s2) {
@@ -396,7 +445,7 @@ MOE_DEV void pin_acc(v16f (&acc)[FH][2]) {
 struct NoSideWork {
   static constexpr bool kEnabled = false;
   MOE_DEV bool wants(int) const { return false; }
-  MOE_DEV void run(const uint8_t*, int) {}
+  MOE_DEV void run(const uint8_t*, const uint8_t*, int) {}
 };
 
 // acc = this wave's part of A_tile * B_tile^T over K = 128 nk; one barrier per stage.
@@ -414,17 +463,19 @@ MOE_DEV void mainloop8(uint8_t* lds, const TileLoads8<F>& L, int nk, v16f (&acc)
     acc[m][1] = (v16f){};
   });
   if (nk <= 0) return;
-  issue_stage8<F>(L, lds, 0);
+  // group row 64w + l's scale offset (read back by the same wave only: no barrier needed)
+  sg_table(lds)[threadIdx.x] = L.sc;
+  issue_stage8<F>(L, lds, 0, nk);
   for (int t = 0; t < nk; ++t) {
     wait_loads_and_sync<0>();  // stage t has landed; every wave is done with stage t - 1
-    if (t + 1 < nk) issue_stage8<F>(L, lds, t + 1);
+    if (t + 1 < nk) issue_stage8<F>(L, lds, t + 1, nk);
     if constexpr (std::remove_reference_t<Side>::kEnabled) {
       // the previous stage's matrix instructions are issued before the side work (a branch
       // could otherwise let the compiler sink them past it)
       pin_acc<(F + 1) / 2>(acc);
-      if (side.wants(t)) side.run((const uint8_t*)(lds + (t % 2) * STAGE_BYTES), t);
+      if (side.wants(t)) side.run((const uint8_t*)(lds + (t % 2) * STAGE_BYTES), sg_buf(lds, t), t);
     }
-    compute_stage8<F>(lds + (t % 2) * STAGE_BYTES, acc);
+    compute_stage8<F>(lds + (t % 2) * STAGE_BYTES, sg_buf(lds, t), t, acc);
   }
 }
 
@@ -476,14 +527,14 @@ struct RequantT8 {
   }
 
   // requantise staged stage t (K columns [128t, 128t + 128)) and store it
-  MOE_DEV void run(const uint8_t* st, int t) {
+  MOE_DEV void run(const uint8_t* st, const uint8_t* sg, int t) {
     if (obase < 0) return;  // wave-uniform
     const int w = threadIdx.x >> 6, l = lane_id();
     const int hf = w >> 2, cq = w & 3, rg = l & 15, cgp = l >> 4;
     // the lane's 8 rows are staged rows r0 .. r0 + 8 (a multiple of 8: they share swz's high part)
     const int r0 = staged(hf, 8 * rg);
     float f[8];  // the rows' scales as conversion operands (one K block per wave: block cq)
-    static_for<8>([&]<int j>() { f[j] = e8m0_operand(st[DATA_BYTES + TM * 4 + 4 * (r0 + j) + cq]); });
+    static_for<8>([&]<int j>() { f[j] = e8m0_operand(sg[sg_pos(TM + r0 + j, t) + cq]); });
     int ld = ldt;
     // opaque per call: keeps the compiler from hoisting the columns' addresses out of the GEMM's
     // K loop, where they would stay live (and spill) across the matrix work
