@@ -229,7 +229,11 @@ def main() -> int:
     ap.add_argument("--flags", type=int, default=0, help="moe_config.flags (2 = ring dispatch)")
     ap.add_argument("--forward-only", action="store_true",
                     help="time moe_fwd alone (MOE_F_FORWARD_ONLY: no state saved for a backward pass)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="the unfused forward baseline (MOE_F_UNFUSED; implies --forward-only)")
     args = ap.parse_args()
+    if args.unfused:
+        args.forward_only = True
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one MI355X: the layer runs with every expert resident on a single GPU; "
               "it has no multi-GPU mode (use --gpus 1).", file=sys.stderr)
@@ -246,7 +250,7 @@ def main() -> int:
     cfg = moe_inputs.CONFIGS[args.config].with_(backward=not fwd_only)
     if args.tokens:
         cfg = cfg.with_(T=args.tokens, name=f"{cfg.name}_T{args.tokens}")
-    flags = args.flags | (moe.MOE_F_FORWARD_ONLY if fwd_only else 0)
+    flags = args.flags | (moe.MOE_F_FORWARD_ONLY if fwd_only else 0) | (moe.MOE_F_UNFUSED if args.unfused else 0)
     t0 = time.time()
     inp = moe_inputs.layer_inputs(cfg, with_dy=not fwd_only)
     layer = MoeLayer.from_config(cfg, with_backward=not fwd_only, flags=flags)
@@ -374,7 +378,8 @@ def main() -> int:
                                 f"E={cfg.E}{f'+{cfg.n_shared} shared' if cfg.n_shared else ''} k={cfg.k} "
                                 f"I={cfg.inter} {cfg.score}, seed {cfg.seed}"),
                    "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "inter": cfg.inter, "score": cfg.score,
-                   "n_shared": cfg.n_shared, "seed": cfg.seed, "parallelism": "single GPU"},
+                   "n_shared": cfg.n_shared, "seed": cfg.seed, "parallelism": "single GPU",
+                   "path": "unfused" if args.unfused else "fused"},
         "tflops": round(tflops, 2),
         "mfma_frac_layer": round(flops_gemm / (ms * 1e-3) / MXFP8_PEAK, 4),
         "mfma_frac_gemms": round(flops_gemm / (gemm_ms * 1e-3) / MXFP8_PEAK, 4),

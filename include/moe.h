@@ -111,6 +111,18 @@ typedef struct moe_config {
  * flag with MOE_EINVAL. */
 #define MOE_F_FORWARD_ONLY 16u
 
+/* The unfused forward: the same arithmetic as the default forward, bit for bit, as the
+ * conventional pipeline of separate kernels with a trip through HBM at every boundary (route,
+ * permute, expert GEMMs, activation, unpermute, combine: commentary "Cursor 开源 MoK…", sections
+ * 瓶颈的真正来源 and 两份成绩单), kept as the in-house baseline that measures what the fused forward
+ * buys: a permute pass gathers the quantised rows into expert order, the gate/up GEMM reads them
+ * contiguously and stores G and U, a separate pass applies SwiGLU and quantises H, the down GEMM
+ * writes its rows in expert order and an unpermute pass moves them to their (token, slot) rows
+ * before the combine.  Needs MOE_F_FORWARD_ONLY and T*(k + n_shared)*d < 2^32 (else MOE_EINVAL /
+ * MOE_ESHAPE); the workspace then holds the permuted rows (moe_workspace_layout xp, xps, yrows).
+ * moe_fwd_noalloc rejects it (MOE_EINVAL). */
+#define MOE_F_UNFUSED 32u
+
 /* Byte offsets inside the caller-owned `saved` buffer that moe_fwd fills and moe_bwd reads
  * (the schedule is built once and reused by the backward pass: knowledge card, 方法/产品要点).
  * R = T*k routed rows, RS = R + n_shared*T rows in expert-major ("permuted") order,
@@ -165,6 +177,9 @@ typedef struct moe_workspace_layout {
   size_t dyts;       /* e8m0  [d, ld/32] */
   size_t dgut;       /* fp8   [2I, ld]     [dG dU], same */
   size_t dguts;      /* e8m0  [2I, ld/32] */
+  size_t xp;         /* fp8   [RS, d]      quantised rows in expert order (MOE_F_UNFUSED only, else empty) */
+  size_t xps;        /* e8m0  [RS, d/32] */
+  size_t yrows;      /* float [RS, d]      down GEMM rows in expert order (MOE_F_UNFUSED only) */
   size_t tok_stride; /* ld: tokens per row of the token-axis operands (a size, not an offset);
                         expert e occupies columns [tok_off[e], tok_off[e + 1]) */
   size_t total;      /* bytes of `workspace` */

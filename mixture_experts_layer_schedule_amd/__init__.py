@@ -20,6 +20,7 @@ MOE_F_RING_DISPATCH = 2
 MOE_F_SERIAL_BWD = 4
 MOE_F_IDENTITY_EXPERTS = 8
 MOE_F_FORWARD_ONLY = 16
+MOE_F_UNFUSED = 32
 MOE_DEV_RING_TIMEOUT, MOE_DEV_NONFINITE_LOGIT = 1, 2
 
 # every symbol include/moe.h declares
@@ -49,7 +50,8 @@ class moe_saved_layout(ctypes.Structure):
 class moe_workspace_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "status", "ring", "ring_s", "ring_flags", "blkcnt", "dyq", "dys", "dw", "dl", "dguq", "dgus", "dxslot",
-        "xt", "xts", "ht", "hts", "dyt", "dyts", "dgut", "dguts", "tok_stride", "total")]
+        "xt", "xts", "ht", "hts", "dyt", "dyts", "dgut", "dguts", "xp", "xps", "yrows", "tok_stride",
+        "total")]
 
 
 class MoeError(RuntimeError):

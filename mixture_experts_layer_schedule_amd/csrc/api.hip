@@ -16,6 +16,7 @@ size_t up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 struct Dims {
   int64_t T, d, E, k, I, S, NX, R, RS, nblk, ld_tok, tiles_bound, tile64_bound;
   int64_t nslots, producers;
+  bool unfused;
 };
 
 constexpr int kChunkRows = 256;      // rows per ring slot: one GEMM row tile at most
@@ -37,11 +38,13 @@ Dims dims(const moe_config& c) {
   const int64_t ring_rows = !(c.flags & MOE_F_RING_DISPATCH) ? 0 : c.ring_rows ? c.ring_rows : kDefaultRingRows;
   m.nslots = ring_rows / kChunkRows;
   m.producers = c.producer_wgs ? c.producer_wgs : kDefaultProducers;
+  m.unfused = (c.flags & MOE_F_UNFUSED) != 0;
   return m;
 }
 
 constexpr uint32_t kKnownFlags =
-    MOE_F_DIRECT_GATHER | MOE_F_RING_DISPATCH | MOE_F_SERIAL_BWD | MOE_F_IDENTITY_EXPERTS | MOE_F_FORWARD_ONLY;
+    MOE_F_DIRECT_GATHER | MOE_F_RING_DISPATCH | MOE_F_SERIAL_BWD | MOE_F_IDENTITY_EXPERTS | MOE_F_FORWARD_ONLY |
+    MOE_F_UNFUSED;
 
 moe_status check_config(const moe_config* c) {
   if (!c) return MOE_EINVAL;
@@ -65,6 +68,11 @@ moe_status check_config(const moe_config* c) {
   if ((int64_t)c->T * c->d >= (1ll << 32)) return MOE_ESHAPE;
   if (2 * (int64_t)c->inter * c->d >= (1ll << 32)) return MOE_ESHAPE;
   if (dims(*c).ld_tok >= (1ll << 24)) return MOE_ESHAPE;
+  if (c->flags & MOE_F_UNFUSED) {
+    // the forward baseline only (no transposed weights for a backward pass), with real experts
+    if (!(c->flags & MOE_F_FORWARD_ONLY) || (c->flags & MOE_F_IDENTITY_EXPERTS)) return MOE_EINVAL;
+    if (RS * c->d >= (1ll << 32)) return MOE_ESHAPE;  // the permuted rows, one 32-bit offset base
+  }
   return MOE_OK;
 }
 
@@ -132,6 +140,9 @@ moe_workspace_layout work_layout(const Dims& m) {
   w.dyts = L.take(m.d * m.ld_tok / 32);
   w.dgut = L.take(2 * m.I * m.ld_tok);
   w.dguts = L.take(2 * m.I * m.ld_tok / 32);
+  w.xp = L.take(m.unfused ? m.RS * m.d : 0);
+  w.xps = L.take(m.unfused ? m.RS * m.d / 32 : 0);
+  w.yrows = L.take(m.unfused ? 4 * m.RS * m.d : 0);
   w.tok_stride = (size_t)m.ld_tok;
   w.total = L.off;
   return w;
@@ -237,6 +248,8 @@ struct FwdScratch {
   int32_t* blkcnt;      // [ceil(T/64), E] per-block expert counts
   uint8_t *ring, *ring_s;
   int32_t* ring_flags;
+  uint8_t *xp = nullptr, *xps = nullptr;  // unfused forward: rows in expert order
+  float* yrows = nullptr;
 };
 
 moe_status forward_impl(const moe_config* cfg, const Dims& m, const moe_saved_layout& sl, const void* x,
@@ -291,7 +304,44 @@ moe_status forward_impl(const moe_config* cfg, const Dims& m, const moe_saved_la
   }
 
   const SchedView sv = sched_view(saved, sl, m);
-  GateUpArgs ga;
+  if (m.unfused) {
+    // the conventional pipeline: permute, gate/up GEMM (G, U), SwiGLU + quantisation, down GEMM
+    // (rows in expert order), unpermute, combine; every boundary through HBM
+    MOE_TRY(launch_permute_rows(sv, xq, xs, d, (int)m.RS, sc.xp, sc.xps, stream));
+    GateUpArgs ga{};
+    ga.s = sv;
+    ga.xq = sc.xp;
+    ga.xs = sc.xps;
+    ga.contiguous = 1;
+    ga.w1q = w1q;
+    ga.w1s = w1s;
+    ga.g = at<float>(saved, sl.g);
+    ga.u = at<float>(saved, sl.u);
+    ga.d = d;
+    ga.I = I;
+    MOE_TRY(launch_gemm_gateup(ga, (int)m.tiles_bound, stream));
+    mark(stream, MOE_PH_GATEUP);
+    uint8_t* hq = at<uint8_t>(saved, sl.hq);
+    uint8_t* hs = at<uint8_t>(saved, sl.hs);
+    MOE_TRY(launch_swiglu_quant(ga.g, ga.u, (int)m.RS, I, hq, hs, stream));
+    DownArgs da{};
+    da.s = sv;
+    da.hq = hq;
+    da.hs = hs;
+    da.w2q = w2q;
+    da.w2s = w2s;
+    da.yrows = sc.yrows;
+    da.d = d;
+    da.I = I;
+    MOE_TRY(launch_gemm_down(da, (int)m.tiles_bound, stream));
+    float* yslot = at<float>(saved, sl.yslot);
+    MOE_TRY(launch_unpermute_rows(sv, sc.yrows, (int)m.RS, d, yslot, stream));
+    mark(stream, MOE_PH_DOWN);
+    MOE_TRY(launch_combine(yslot, w, (int)m.T, (int)m.k, (int)m.S, d, (uint16_t*)y_bf16, y_f32, stream));
+    mark(stream, MOE_PH_COMBINE);
+    return MOE_OK;
+  }
+  GateUpArgs ga{};
   ga.s = sv;
   ga.xq = xq;
   ga.xs = xs;
@@ -336,7 +386,7 @@ moe_status forward_impl(const moe_config* cfg, const Dims& m, const moe_saved_la
   }
   mark(stream, MOE_PH_GATEUP);
 
-  DownArgs da;
+  DownArgs da{};
   da.s = sv;
   da.hq = ga.hq;
   da.hs = ga.hs;
@@ -409,6 +459,11 @@ moe_status moe_fwd(const moe_config* cfg, const void* x, const void* w_router, c
   sc.ring = at<uint8_t>(workspace, wl.ring);
   sc.ring_s = at<uint8_t>(workspace, wl.ring_s);
   sc.ring_flags = at<int32_t>(workspace, wl.ring_flags);
+  if (m.unfused) {
+    sc.xp = at<uint8_t>(workspace, wl.xp);
+    sc.xps = at<uint8_t>(workspace, wl.xps);
+    sc.yrows = at<float>(workspace, wl.yrows);
+  }
   return forward_impl(cfg, m, sl, x, w_router, router_bias, w1q, w1s, w2q, w2s, y_bf16, y_f32, saved, sc, stream);
 }
 
@@ -417,7 +472,8 @@ moe_status moe_fwd_noalloc(const moe_config* cfg, const void* x, const void* w_r
                            void* y_bf16, float* y_f32, void* saved, size_t saved_bytes, hipStream_t stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
-  if (cfg->flags & MOE_F_RING_DISPATCH) return MOE_EINVAL;  // the ring buffer lives in a workspace
+  // the ring buffer and the unfused forward's permuted rows live in a workspace
+  if (cfg->flags & (MOE_F_RING_DISPATCH | MOE_F_UNFUSED)) return MOE_EINVAL;
   if (!x || !w_router || !w1q || !w1s || !w2q || !w2s || !y_bf16 || !saved) return MOE_EINVAL;
   if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(w1q, 16) || !aligned(w2q, 16) || !aligned(y_bf16, 16) ||
       (y_f32 && !aligned(y_f32, 16)) || !aligned(saved, kAlign))

@@ -71,15 +71,25 @@ __global__ __launch_bounds__(512, 1) void k_gemm_gateup(GateUpArgs p) {
   side.obase = ((threadIdx.x >> 8) ? I : 0) + n0;
   side.m = rt.m;
   side.nm = rt.nm;
+  // A row of staged row r: the token of permuted row r0 + r (pull dispatch), or with
+  // `contiguous` that permuted row itself (rows already in expert order)
+  const bool cont = p.contiguous != 0;
+  auto arow = [&](int r) {
+    const int rr = rt.r0 + min(r, last);
+    return cont ? rr : row_token(s, rr);
+  };
   dispatch_rows(rt.rows, [&]<int F>() {
     TileLoads8<F> L;
-    L.init(p.xq, [&](int r) { return p.xq + (size_t)row_token(s, rt.r0 + min(r, last)) * d; },
+    L.init(p.xq, [&](int r) { return p.xq + (size_t)arow(r) * d; },
            w1, [&](int r) { return w1 + (size_t)gateup_brow(r, n0, I) * d; },
-           p.xs, [&](int r) { return p.xs + (size_t)row_token(s, rt.r0 + min(r, last)) * (d / 32); },
+           p.xs, [&](int r) { return p.xs + (size_t)arow(r) * (d / 32); },
            w1s, [&](int r) { return w1s + (size_t)gateup_brow(r, n0, I) * (d / 32); });
     v16f acc[(F + 1) / 2][2];
     mainloop8<F>(lds, L, d / KS, acc, side);
-    gateup_epilogue8<F>(acc, rt.r0, rt.rows, n0, I, p.g, p.u, p.hq, p.hs);
+    if (p.hq)
+      gateup_epilogue8<F>(acc, rt.r0, rt.rows, n0, I, p.g, p.u, p.hq, p.hs);
+    else
+      gu_store8<F>(acc, rt.r0, rt.rows, n0, I, p.g, p.u);
   });
 }
 
@@ -122,6 +132,20 @@ __global__ __launch_bounds__(512, 1) void k_gemm_down(DownArgs p) {
            w2s, [&](int r) { return w2s + (size_t)min(n0 + r, d - 1) * (I / 32); });
     v16f acc[FH][2];
     mainloop8<F>(lds, L, I / KS, acc, side);
+    if (p.yrows) {  // the unfused forward: rows stay in expert order
+      if (!active) return;
+      static_for<FH>([&]<int m>() {
+        static_for<16>([&]<int v>() {
+          const int r = 32 * (m0 + m) + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (r < rt.rows) {
+            float* dst = p.yrows + (size_t)(rt.r0 + r) * d + n0 + 64 * wc + i;
+            dst[0] = acc[m][0][v];
+            dst[32] = acc[m][1][v];
+          }
+        });
+      });
+      return;
+    }
     const int64_t* slot = row_slot_table(s, rt, lds + ((I / KS) % kStages) * STAGE_BYTES);
     if (!active) return;
     static_for<FH>([&]<int m>() {

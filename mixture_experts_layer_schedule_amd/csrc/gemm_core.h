@@ -664,6 +664,27 @@ MOE_DEV void gateup_epilogue8(const v16f (&acc)[(F + 1) / 2][2], int r0, int row
   });
 }
 
+// G and U of the 8-wave gate/up tile stored without the activation (the unfused forward applies
+// SwiGLU and the quantisation in a pass of its own).
+template <int F>
+MOE_DEV void gu_store8(const v16f (&acc)[(F + 1) / 2][2], int r0, int rows, int n0, int I, float* g_out,
+                       float* u_out) {
+  constexpr int FH = (F + 1) / 2;
+  const int l = lane_id(), i = l & 31, h = l >> 5, w = threadIdx.x >> 6;
+  const int wc = w & 3, m0 = (w >> 2) * FH;
+  const int n = n0 + 32 * wc + i;
+  static_for<FH>([&]<int m>() {
+    static_for<16>([&]<int v>() {
+      const int r = 32 * (m0 + m) + 8 * (v >> 2) + 4 * h + (v & 3);
+      if (r < rows) {
+        const size_t o = (size_t)(r0 + r) * I + n;
+        g_out[o] = acc[m][0][v];
+        u_out[o] = acc[m][1][v];
+      }
+    });
+  });
+}
+
 // B rows of a gate/up tile: staged row r of wave r / 64 is gate row n0 + 32(r / 64) + r % 32
 // for r % 64 < 32, else the matching up row (I further on).
 MOE_DEV int gateup_brow(int r, int n0, int I) {

@@ -20,17 +20,20 @@ struct SchedView {
 
 struct GateUpArgs {
   SchedView s;
-  const uint8_t *xq, *xs, *w1q, *w1s;
+  const uint8_t *xq, *xs, *w1q, *w1s;  // xq, xs: [T, d] gathered through the schedule, or with
+                                       // `contiguous` [RS, d] already in expert order
   float *g, *u;
-  uint8_t *hq, *hs;
+  uint8_t *hq, *hs;     // NULL with `contiguous`: G and U only (the unfused forward)
   uint8_t *w1t, *w1ts;  // [NX][d][2I] + [NX][2I/128][d][4]: W1 transposed, requantised along 2I (NULL: skip)
   int d, I;
+  int contiguous;
 };
 
 struct DownArgs {
   SchedView s;
   const uint8_t *hq, *hs, *w2q, *w2s;
-  float* yslot;
+  float* yslot;          // each row pushed to its (token, slot) row
+  float* yrows;          // or, when not NULL, [RS, d] rows in expert order (the unfused forward)
   uint8_t *w2t, *w2ts;  // [NX][I][d] + [NX][d/128][I][4]: W2 transposed, requantised along d (NULL: skip)
   int d, I;
 };
@@ -86,6 +89,13 @@ hipError_t launch_gemm_dgrad_down(const DgradDownArgs&, int tiles_bound, hipStre
 hipError_t launch_gemm_dgrad_gateup(const DgradGateUpArgs&, int tiles_bound, hipStream_t);
 // which: 0 for dW2, 1 for dW1 (separate kernel names in traces)
 hipError_t launch_gemm_wgrad(const WgradArgs&, int which, hipStream_t);
+
+// The unfused forward's own passes: xp[r] = xq[token of permuted row r] (codes and scales);
+// H = quantise(silu(G) U) along I; yslot[slot of row r] = yrows[r].
+hipError_t launch_permute_rows(const SchedView& s, const uint8_t* xq, const uint8_t* xs, int d, int RS, uint8_t* xp,
+                               uint8_t* xps, hipStream_t);
+hipError_t launch_swiglu_quant(const float* g, const float* u, int RS, int I, uint8_t* hq, uint8_t* hs, hipStream_t);
+hipError_t launch_unpermute_rows(const SchedView& s, const float* yrows, int RS, int d, float* yslot, hipStream_t);
 
 // MXFP8 quantisation along the contiguous axis of a [rows, cols] bf16 (src_f32 = 0) or
 // float32 (src_f32 = 1) matrix.

@@ -124,6 +124,7 @@ class MoeLayer:
             "ht": (torch.uint8, (I, ld)), "hts": (torch.uint8, (I, ld // 32)),
             "dyt": (torch.uint8, (d, ld)), "dyts": (torch.uint8, (d, ld // 32)),
             "dgut": (torch.uint8, (2 * I, ld)), "dguts": (torch.uint8, (2 * I, ld // 32)),
+            "xp": (torch.uint8, (RS, d)), "xps": (torch.uint8, (RS, d // 32)), "yrows": (torch.float32, (RS, d)),
         }
         dt, shape = spec[name]
         off = getattr(self.wlayout, name)

@@ -281,3 +281,26 @@ def test_forward_only_matches_default_forward():
     assert torch.equal(a.y32, b.y32) and torch.equal(a.y, b.y)
     for name in ("hq", "hs", "g", "u", "yslot", "perm"):
         assert torch.equal(a.saved_tensor(name), b.saved_tensor(name)), name
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
+def test_unfused_forward_matches_fused_forward(cfg):
+    """The unfused forward (permute, GEMM, SwiGLU pass, GEMM, unpermute, combine through HBM) is the
+    in-house baseline of the fused forward: same arithmetic, so the same bits in every output and
+    saved activation."""
+    import torch
+    import mixture_experts_layer_schedule_amd as moe
+    inp = moe_inputs.layer_inputs(cfg, with_dy=False)
+    ws = [moe_inputs.expert_weights(cfg, e) for e in range(cfg.E + cfg.n_shared)]
+    fo = moe.MOE_F_FORWARD_ONLY
+    a = gpu_layer(cfg, False, inp=inp, ws=ws, flags=fo)
+    b = gpu_layer(cfg, False, inp=inp, ws=ws, flags=fo | moe.MOE_F_UNFUSED)
+    assert torch.equal(a.y32, b.y32) and torch.equal(a.y, b.y)
+    for name in ("g", "u", "hq", "hs", "yslot", "perm", "xq"):
+        assert torch.equal(a.saved_tensor(name), b.saved_tensor(name)), name
+    # the permuted rows are the schedule's gather of xq
+    perm = b.saved_tensor("perm").long()
+    R = cfg.T * cfg.k
+    toks = torch.cat([perm // cfg.k, torch.arange(cfg.T, device=perm.device).repeat(cfg.n_shared)])
+    assert torch.equal(b.workspace_tensor("xp"), a.saved_tensor("xq")[toks])
+    assert R + cfg.n_shared * cfg.T == toks.numel()

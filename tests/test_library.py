@@ -74,7 +74,11 @@ def test_forward_only_layout_drops_transposed_weights():
     (dict(producer_wgs=8), moe.MOE_EINVAL),
     (dict(flags=2), moe.MOE_EINVAL),         # ring dispatch is disabled
     (dict(flags=3), moe.MOE_EINVAL),         # direct gather and ring dispatch together
-    (dict(flags=32), moe.MOE_EINVAL),        # unknown flag
+    (dict(flags=64), moe.MOE_EINVAL),        # unknown flag
+    (dict(flags=32), moe.MOE_EINVAL),        # the unfused forward needs MOE_F_FORWARD_ONLY
+    (dict(flags=32 | 16 | 8), moe.MOE_EINVAL),  # ... and real experts
+    # the unfused forward's permuted rows: T * (k + S) * d reaches 2^32
+    (dict(T=(1 << 32) // (7168 * 2) + 1, d=7168, E=8, k=2, inter=128, flags=48), moe.MOE_ESHAPE),
     # 32-bit operand offsets: T * d reaches 2^32
     (dict(T=(1 << 32) // 7168 + 1, d=7168, E=8, k=1, inter=128), moe.MOE_ESHAPE),
     # one expert's weights 2 * I * d reach 2^32
@@ -99,11 +103,34 @@ def test_query_accepts_sizes_just_inside_the_limits():
     moe.moe_query(moe.make_config(1 << 19, 128, 16, 16, 128))                 # stride < 2^24
 
 
-@pytest.mark.parametrize("flags", [0, 1, 4, 5, 8, 9, 16, 20])
+@pytest.mark.parametrize("flags", [0, 1, 4, 5, 8, 9, 16, 20, 48, 49])
 def test_query_accepts_schedule_flags(flags):
-    """Direct gather (1), the launch-order backward (4), identity experts (8) and forward only (16)."""
+    """Direct gather (1), the launch-order backward (4), identity experts (8), forward only (16) and
+    the unfused forward (32 with 16)."""
     ws, _ = moe.moe_query(moe.make_config(256, 256, 8, 2, 128, flags=flags))
     assert ws > 0
+
+
+def test_unfused_layout_holds_the_permuted_rows():
+    T, d, E, k, I = 256, 256, 8, 2, 128
+    RS = T * k
+    _, fo, wfo = moe.moe_query(moe.make_config(T, d, E, k, I, flags=moe.MOE_F_FORWARD_ONLY), with_workspace_layout=True)
+    _, uf, wuf = moe.moe_query(moe.make_config(T, d, E, k, I, flags=moe.MOE_F_FORWARD_ONLY | moe.MOE_F_UNFUSED),
+                               with_workspace_layout=True)
+    assert uf.total == fo.total  # the saved state is the fused forward's
+    assert wfo.xp == wfo.xps == wfo.yrows and wfo.yrows <= wfo.total
+    assert wuf.xps - wuf.xp >= RS * d and wuf.yrows - wuf.xps >= RS * d // 32
+    assert wuf.total - wuf.yrows >= 4 * RS * d
+
+
+def test_noalloc_forward_rejects_workspace_modes():
+    """The ring dispatch and the unfused forward need a workspace: refused before any launch."""
+    p, big = 1 << 20, 1 << 40
+    for flags in (moe.MOE_F_FORWARD_ONLY | moe.MOE_F_UNFUSED,):
+        cfg = moe.make_config(256, 256, 8, 2, 128, flags=flags)
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_fwd_noalloc(cfg, p, p, None, p, p, p, p, p, None, p, stream=0, saved_bytes=big)
+        assert ei.value.status == moe.MOE_EINVAL
 
 
 def test_forward_rejects_null_and_misaligned_pointers_without_launching():
