@@ -324,6 +324,14 @@ def main() -> int:
 
     tok_off = layer.saved_tensor("tok_off").cpu().numpy()
     work = phase_work(cfg, int(tok_off[-1]), backward=not fwd_only)
+    # the grouped GEMMs' work items: row tiles (up to 256 rows of one expert) x column tiles
+    counts = layer.saved_tensor("counts").cpu().numpy()
+    row_tiles = int(layer.saved_tensor("tile_start").cpu().numpy()[-1])
+    col_tiles = {"gateup": cfg.inter // 128, "down": -(-cfg.d // 256), "dgrad_down": -(-cfg.inter // 256),
+                 "dgrad_gateup": -(-cfg.d // 256)}
+    sched = {"rows_per_expert_mean": round(float(counts.mean()), 1), "rows_per_expert_max": int(counts.max()),
+             "empty_experts": int((counts == 0).sum()), "row_tiles": row_tiles,
+             "tiles": {g: row_tiles * n for g, n in col_tiles.items()}}
     gemms = ("gateup", "down") if fwd_only else ("gateup", "down", "dgrad_down", "dgrad_gateup", "wgrad_down",
                                                  "wgrad_gateup")
     flops_fwd = sum(work[p][0] for p in ("gateup", "down"))
@@ -386,6 +394,7 @@ def main() -> int:
         "fwd_tflop": round(flops_fwd / 1e12, 3),
         "ms_per_step_launch_order": round(ms_serial, 4),
         "phases": phases,
+        "schedule": sched,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

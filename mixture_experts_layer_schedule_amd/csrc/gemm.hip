@@ -166,7 +166,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_down(DownArgs p) {
 // dH = w * (dY_t W2t_e^T) (rows pulled from dYq: reverse-combine), dG = dH U s (1 + G (1 - s)),
 // dU = dH silu(G); [dG dU] quantised along 2I.
 
-__global__ __launch_bounds__(256, 1) void k_gemm_dgrad_down(DgradDownArgs p) {
+__global__ __launch_bounds__(512, 1) void k_gemm_dgrad_down(DgradDownArgs p) {
   extern __shared__ __align__(16) uint8_t lds[];
   const SchedView& s = p.s;
   const int I = p.I, d = p.d, NT = (I + TN - 1) / TN;
@@ -177,33 +177,36 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_down(DgradDownArgs p) {
   if (rt.rows <= 0) return;
   const int n0 = nt * TN;
   const int last = rt.rows - 1;
-  const int w = threadIdx.x >> 6, l = lane_id(), i = l & 31, h = l >> 5;
-  const bool active = n0 + 64 * w < I;
+  const int w = threadIdx.x >> 6, l = lane_id(), i = l & 31, h = l >> 5, wc = w & 3;
+  const bool active = n0 + 64 * wc < I;
   const uint8_t* w2t = p.w2t + (size_t)rt.e * I * d;  // W2^T [I][d], quantised along d; scales [d/128][I] words
   const uint8_t* w2ts = p.w2ts + (size_t)rt.e * I * (d / 32);
   dispatch_rows(rt.rows, [&]<int F>() {
-    TileLoads<F> L;
+    constexpr int FH = (F + 1) / 2;
+    const int m0 = (w >> 2) * FH;
+    TileLoads8<F> L;
     L.init(p.dyq, [&](int r) { return p.dyq + (size_t)row_token(s, rt.r0 + min(r, last)) * d; },
            w2t, [&](int r) { return w2t + (size_t)min(n0 + r, I - 1) * d; },
            p.dys, [&](int r) { return p.dys + (size_t)row_token(s, rt.r0 + min(r, last)) * (d / 32); },
            w2ts, [&](int r) { return w2ts + (size_t)min(n0 + r, I - 1) * 4; });
-    L.bsk = 4 * I;  // word-major scales: stage t's words are plane t
-    v16f acc[F][2];
-    mainloop<F, 2, 0, false>(lds, L, d / KS, acc);
+    L.bsk = 4 * I;  // stage-major scales: stage t's words are plane t
+    v16f acc[FH][2];
+    mainloop8<F, false>(lds, L, d / KS, acc);
     // combine weight of every row of the tile, once, through LDS
     float* wt = (float*)(lds + ((d / KS) % kStages) * STAGE_BYTES);
     if ((int)threadIdx.x < rt.rows) wt[threadIdx.x] = row_weight(s, p.w, rt.r0 + threadIdx.x);
     __syncthreads();
     if (!active) return;
     const int I2 = 2 * I;
-    static_for<F>([&]<int mi>() {
+    static_for<FH>([&]<int m>() {
+      const int mi = m0 + m;
       // G and U of the fragment's 16 rows x 2 columns first: their loads overlap
       float gv[2][16], uv[2][16], wv[16];
       static_for<16>([&]<int v>() {
         const int rg = rt.r0 + min(32 * mi + 8 * (v >> 2) + 4 * h + (v & 3), last);
         wv[v] = wt[rg - rt.r0];
         static_for<2>([&]<int ni>() {
-          const size_t o = (size_t)rg * I + n0 + 64 * w + 32 * ni + i;
+          const size_t o = (size_t)rg * I + n0 + 64 * wc + 32 * ni + i;
           gv[ni][v] = p.g[o];
           uv[ni][v] = p.u[o];
         });
@@ -212,9 +215,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_down(DgradDownArgs p) {
         const int r = 32 * mi + 8 * (v >> 2) + 4 * h + (v & 3);
         const int rg = rt.r0 + min(r, last);
         static_for<2>([&]<int ni>() {
-          const int n = n0 + 64 * w + 32 * ni + i;
+          const int n = n0 + 64 * wc + 32 * ni + i;
           const float g = gv[ni][v], u = uv[ni][v];
-          const float dh = wv[v] * acc[mi][ni][v];
+          const float dh = wv[v] * acc[m][ni][v];
           const float sg = sigmoid(g);
           const float dg = dh * u * sg * (1.0f + g * (1.0f - sg));
           const float du = dh * g * sg;
@@ -241,7 +244,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_down(DgradDownArgs p) {
 // Backward dgrad of the gate/up GEMM: dX_r = dGU_r W1t_e^T, pushed to dXslot[t, j]
 // (push reverse-dispatch).
 
-__global__ __launch_bounds__(256, 1) void k_gemm_dgrad_gateup(DgradGateUpArgs p) {
+__global__ __launch_bounds__(512, 1) void k_gemm_dgrad_gateup(DgradGateUpArgs p) {
   extern __shared__ __align__(16) uint8_t lds[];
   const SchedView& s = p.s;
   const int I2 = 2 * p.I, d = p.d, NT = (d + TN - 1) / TN;
@@ -252,30 +255,32 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dgrad_gateup(DgradGateUpArgs p)
   if (rt.rows <= 0) return;
   const int n0 = nt * TN;
   const int last = rt.rows - 1;
-  const int w = threadIdx.x >> 6, l = lane_id(), i = l & 31, h = l >> 5;
-  const bool active = n0 + 64 * w < d;
+  const int w = threadIdx.x >> 6, l = lane_id(), i = l & 31, h = l >> 5, wc = w & 3;
+  const bool active = n0 + 64 * wc < d;
   const uint8_t* w1t = p.w1t + (size_t)rt.e * d * I2;  // W1^T [d][2I], quantised along 2I; scales [2I/128][d] words
   const uint8_t* w1ts = p.w1ts + (size_t)rt.e * d * (I2 / 32);
   dispatch_rows(rt.rows, [&]<int F>() {
-    TileLoads<F> L;
+    constexpr int FH = (F + 1) / 2;
+    const int m0 = (w >> 2) * FH;
+    TileLoads8<F> L;
     const uint8_t* ga = p.dguq + (size_t)rt.r0 * I2;
     const uint8_t* gsa = p.dgus + (size_t)rt.r0 * (I2 / 32);
     L.init(ga, [&](int r) { return ga + (size_t)min(r, last) * I2; },
            w1t, [&](int r) { return w1t + (size_t)min(n0 + r, d - 1) * I2; },
            gsa, [&](int r) { return gsa + (size_t)min(r, last) * (I2 / 32); },
            w1ts, [&](int r) { return w1ts + (size_t)min(n0 + r, d - 1) * 4; });
-    L.bsk = 4 * d;  // word-major scales: stage t's words are plane t
-    v16f acc[F][2];
-    mainloop<F, 2, 0, false>(lds, L, I2 / KS, acc);
+    L.bsk = 4 * d;  // stage-major scales: stage t's words are plane t
+    v16f acc[FH][2];
+    mainloop8<F, false>(lds, L, I2 / KS, acc);
     const int64_t* slot = row_slot_table(s, rt, lds + ((I2 / KS) % kStages) * STAGE_BYTES);
     if (!active) return;
-    static_for<F>([&]<int mi>() {
+    static_for<FH>([&]<int m>() {
       static_for<16>([&]<int v>() {
-        const int r = 32 * mi + 8 * (v >> 2) + 4 * h + (v & 3);
+        const int r = 32 * (m0 + m) + 8 * (v >> 2) + 4 * h + (v & 3);
         if (r < rt.rows) {
-          float* dst = p.dxslot + slot[r] * d + n0 + 64 * w + i;
-          dst[0] = acc[mi][0][v];
-          dst[32] = acc[mi][1][v];
+          float* dst = p.dxslot + slot[r] * d + n0 + 64 * wc + i;
+          dst[0] = acc[m][0][v];
+          dst[32] = acc[m][1][v];
         }
       });
     });
@@ -342,13 +347,13 @@ hipError_t launch_gemm_down(const DownArgs& a, int tiles_bound, hipStream_t st) 
 }
 
 hipError_t launch_gemm_dgrad_down(const DgradDownArgs& a, int tiles_bound, hipStream_t st) {
-  hipLaunchKernelGGL(k_gemm_dgrad_down, dim3(tiles_bound * ((a.I + TN - 1) / TN)), dim3(256), gemm_lds_bytes(),
+  hipLaunchKernelGGL(k_gemm_dgrad_down, dim3(tiles_bound * ((a.I + TN - 1) / TN)), dim3(512), gemm_lds_bytes(),
                      st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_dgrad_gateup(const DgradGateUpArgs& a, int tiles_bound, hipStream_t st) {
-  hipLaunchKernelGGL(k_gemm_dgrad_gateup, dim3(tiles_bound * ((a.d + TN - 1) / TN)), dim3(256), gemm_lds_bytes(),
+  hipLaunchKernelGGL(k_gemm_dgrad_gateup, dim3(tiles_bound * ((a.d + TN - 1) / TN)), dim3(512), gemm_lds_bytes(),
                      st, a);
   return hipGetLastError();
 }

@@ -350,6 +350,7 @@ struct TileLoads8 {
   uint32_t a[NA];
   uint32_t b[4];
   uint32_t sc;  // A scale word of row 64w + l (w < 4) or B scale word of row 64(w - 4) + l
+  uint32_t bsk = 0;  // stage-major B scales (kGB false): bytes between the planes of successive stages
 
   template <class ARow, class BRow, class ASRow, class BSRow>
   MOE_DEV void init(const uint8_t* ab, ARow a_rows, const uint8_t* bb, BRow b_rows, const uint8_t* asb,
@@ -369,16 +370,20 @@ struct TileLoads8 {
   }
 };
 
-// Loads of stage t into buffer t % 2: one scale word and this wave's share of the data.
-template <int F>
+// Loads of stage t into buffer t % 2: the scales and this wave's share of the data.  kGB: B
+// scales in groups like A's; else (stage-major B scales, a stage's words contiguous) waves 4-7
+// load stage t's word of B rows 64(w - 4) .. every stage.
+template <int F, bool kGB = true>
 MOE_DEV void issue_stage8(const TileLoads8<F>& L, uint8_t* lds, int t, int nk) {
   const int w = threadIdx.x >> 6;
   const uint32_t k0 = (uint32_t)t * KS;
   uint8_t* st = lds + (t % 2) * STAGE_BYTES;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   // scale group: waves 0-3 the A rows 64w .., waves 4-7 the B rows 64(w - 4) .. (group rows 64w ..)
-  if ((t & 3) == 0) {
-    const int wu = __builtin_amdgcn_readfirstlane(w);
-    scale_group<0>(wu < 4 ? L.asbase : L.bsbase, lds, wu, 1024 * wu, t, nk);
+  if (kGB || wu < 4) {
+    if ((t & 3) == 0) scale_group<0>(wu < 4 ? L.asbase : L.bsbase, lds, wu, 1024 * wu, t, nk);
+  } else {
+    lds_load4<0>(L.bsbase + (L.sc + (uint32_t)t * L.bsk), st + DATA_BYTES + TM * 4 + 256 * (wu - 4));
   }
   static_for<TileLoads8<F>::NA>([&]<int u>() {
     const int q = w + 8 * u;
@@ -389,7 +394,7 @@ MOE_DEV void issue_stage8(const TileLoads8<F>& L, uint8_t* lds, int t, int nk) {
 
 // Multiply one staged K slice (two MFMA steps) for this wave's FH row fragments and two column
 // fragments; A fragments read two at a time ahead of the matrix instructions.
-template <int F>
+template <int F, bool kGB = true>
 MOE_DEV void compute_stage8(const uint8_t* st, const uint8_t* sg, int t, v16f (&acc)[(F + 1) / 2][2]) {
   constexpr int FH = (F + 1) / 2;
   const int l = lane_id(), i = l & 31, h = l >> 5, w = threadIdx.x >> 6;
@@ -397,8 +402,14 @@ MOE_DEV void compute_stage8(const uint8_t* st, const uint8_t* sg, int t, v16f (&
   const int sw = swz(i);
   int sa[FH], sb[2];
   static_for<FH>([&]<int m>() { sa[m] = (int)(*(const uint32_t*)(sg + sg_pos(32 * (m0 + m) + i, t)) >> (8 * h)); });
-  sb[0] = (int)(*(const uint32_t*)(sg + sg_pos(TM + 64 * wc + i, t)) >> (8 * h));
-  sb[1] = (int)(*(const uint32_t*)(sg + sg_pos(TM + 64 * wc + 32 + i, t)) >> (8 * h));
+  if constexpr (kGB) {
+    sb[0] = (int)(*(const uint32_t*)(sg + sg_pos(TM + 64 * wc + i, t)) >> (8 * h));
+    sb[1] = (int)(*(const uint32_t*)(sg + sg_pos(TM + 64 * wc + 32 + i, t)) >> (8 * h));
+  } else {
+    const uint32_t* sc = (const uint32_t*)(st + DATA_BYTES);
+    sb[0] = (int)(sc[TM + 64 * wc + i] >> (8 * h));
+    sb[1] = (int)(sc[TM + 64 * wc + 32 + i] >> (8 * h));
+  }
   constexpr int NG = (FH + 1) / 2;
   static_for<2>([&]<int kk>() {
     auto frag = [&](const uint8_t* rp, int s2) {
@@ -455,7 +466,7 @@ struct NoSideWork {
 // (side.run, when side.wants(t)) and then multiplies stage t.  Its stores thus follow the loads
 // of stage t + 1 in issue order and retire while the matrix work runs, so the wait at the top of
 // the next iteration (a wave's memory counter retires in issue order) is not lengthened by them.
-template <int F, class Side = NoSideWork>
+template <int F, bool kGB = true, class Side = NoSideWork>
 MOE_DEV void mainloop8(uint8_t* lds, const TileLoads8<F>& L, int nk, v16f (&acc)[(F + 1) / 2][2],
                        Side&& side = Side{}) {
   static_for<(F + 1) / 2>([&]<int m>() {
@@ -465,17 +476,17 @@ MOE_DEV void mainloop8(uint8_t* lds, const TileLoads8<F>& L, int nk, v16f (&acc)
   if (nk <= 0) return;
   // group row 64w + l's scale offset (read back by the same wave only: no barrier needed)
   sg_table(lds)[threadIdx.x] = L.sc;
-  issue_stage8<F>(L, lds, 0, nk);
+  issue_stage8<F, kGB>(L, lds, 0, nk);
   for (int t = 0; t < nk; ++t) {
     wait_loads_and_sync<0>();  // stage t has landed; every wave is done with stage t - 1
-    if (t + 1 < nk) issue_stage8<F>(L, lds, t + 1, nk);
+    if (t + 1 < nk) issue_stage8<F, kGB>(L, lds, t + 1, nk);
     if constexpr (std::remove_reference_t<Side>::kEnabled) {
       // the previous stage's matrix instructions are issued before the side work (a branch
       // could otherwise let the compiler sink them past it)
       pin_acc<(F + 1) / 2>(acc);
       if (side.wants(t)) side.run((const uint8_t*)(lds + (t % 2) * STAGE_BYTES), sg_buf(lds, t), t);
     }
-    compute_stage8<F>(lds + (t % 2) * STAGE_BYTES, sg_buf(lds, t), t, acc);
+    compute_stage8<F, kGB>(lds + (t % 2) * STAGE_BYTES, sg_buf(lds, t), t, acc);
   }
 }
 
