@@ -1,7 +1,7 @@
 // Grouped MXFP8 GEMMs of the expert FFN (forward, dgrad and wgrad) on gfx950; the tile core is
 // in gemm_core.h.  The routed GEMMs run one (row tile, 256-column tile) item per workgroup; the
-// row count of the item picks the instantiation with that many 32-row fragments.  The forward
-// GEMMs run the tile with 8 waves (two per SIMD, 512 threads), the backward ones with 4.
+// row count of the item picks the instantiation with that many 32-row fragments.  Every GEMM runs
+// the tile with 8 waves (two per SIMD, 512 threads).
 //
 // The forward GEMMs also produce the transposed, requantised weights the backward pass
 // contracts with (W1 along 2I, W2 along d): each stage's staged weight slice is requantised
@@ -292,10 +292,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dgrad_gateup(DgradGateUpArgs p)
 // operands requantised along the token axis and stored token-contiguous at the expert's padded
 // offset.  An expert with no tokens writes zeros.  Tiles are 256 x 256 (128 x 256 when M is not
 // a multiple of 256): the token count is short, so a bigger tile amortises each load latency.
+// They run on the 8-wave core (both operands' scales in groups).
 
 // kWhich only names the launch (0: dW2, 1: dW1) so that traces tell the two GEMMs apart.
 template <int kWgradF, int kWhich>
-__global__ __launch_bounds__(256, 1) void k_gemm_wgrad(WgradArgs p) {
+__global__ __launch_bounds__(512, 1) void k_gemm_wgrad(WgradArgs p) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int MT = p.M / (32 * kWgradF), NT = (p.N + TN - 1) / TN;
   int item;
@@ -305,9 +306,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_wgrad(WgradArgs p) {
   const int K = (int)(p.tok_off[e + 1] - k0);  // multiple of 128
   const int64_t ld = p.ld;                      // token stride of At / Bt rows
   const int m0 = mt * 32 * kWgradF, n0 = nt * TN;
-  const int w = threadIdx.x >> 6, l = lane_id(), i = l & 31, h = l >> 5;
-  const bool active = n0 + 64 * w < p.N;
-  TileLoads<kWgradF> L;
+  const int w = threadIdx.x >> 6, l = lane_id(), i = l & 31, h = l >> 5, wc = w & 3;
+  const bool active = n0 + 64 * wc < p.N;
+  constexpr int FH = (kWgradF + 1) / 2;
+  const int mh = (w >> 2) * FH;
+  TileLoads8<kWgradF> L;
   const uint8_t* at = p.at + (size_t)m0 * ld + k0;
   const uint8_t* bt = p.bt + (size_t)n0 * ld + k0;
   const uint8_t* ats = p.ats + (size_t)m0 * (ld / 32) + k0 / 32;
@@ -316,14 +319,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_wgrad(WgradArgs p) {
          bt, [&](int r) { return bt + (size_t)(min(n0 + r, p.N - 1) - n0) * ld; },
          ats, [&](int r) { return ats + (size_t)min(r, 32 * kWgradF - 1) * (ld / 32); },
          bts, [&](int r) { return bts + (size_t)(min(n0 + r, p.N - 1) - n0) * (ld / 32); });
-  v16f acc[kWgradF][2];
-  mainloop<kWgradF, 2>(lds, L, K / KS, acc);
+  v16f acc[FH][2];
+  mainloop8<kWgradF>(lds, L, K / KS, acc);
   if (!active) return;
   float* out = p.dw + (size_t)e * p.M * p.N;
-  static_for<kWgradF>([&]<int mi>() {
+  static_for<FH>([&]<int mi>() {
     static_for<16>([&]<int v>() {
-      const int m = m0 + 32 * mi + 8 * (v >> 2) + 4 * h + (v & 3);
-      float* dst = out + (size_t)m * p.N + n0 + 64 * w + i;
+      const int m = m0 + 32 * (mh + mi) + 8 * (v >> 2) + 4 * h + (v & 3);
+      float* dst = out + (size_t)m * p.N + n0 + 64 * wc + i;
       __builtin_nontemporal_store(acc[mi][0][v], dst);
       __builtin_nontemporal_store(acc[mi][1][v], dst + 32);
     });
@@ -363,10 +366,10 @@ static hipError_t launch_wgrad(const WgradArgs& a, hipStream_t st) {
   // 256-row tiles when M allows (half the workgroups, each with twice the work per load latency)
   if (a.M % 256 == 0) {
     const int blocks = a.n_exp * (a.M / 256) * ((a.N + TN - 1) / TN);
-    hipLaunchKernelGGL((k_gemm_wgrad<8, kWhich>), dim3(blocks), dim3(256), wgrad_lds_bytes(), st, a);
+    hipLaunchKernelGGL((k_gemm_wgrad<8, kWhich>), dim3(blocks), dim3(512), wgrad_lds_bytes(), st, a);
   } else if (a.M % 128 == 0) {
     const int blocks = a.n_exp * (a.M / 128) * ((a.N + TN - 1) / TN);
-    hipLaunchKernelGGL((k_gemm_wgrad<4, kWhich>), dim3(blocks), dim3(256), wgrad_lds_bytes(), st, a);
+    hipLaunchKernelGGL((k_gemm_wgrad<4, kWhich>), dim3(blocks), dim3(512), wgrad_lds_bytes(), st, a);
   } else {
     return hipErrorInvalidValue;
   }

@@ -330,8 +330,9 @@ MOE_DEV void mainloop(uint8_t* lds, const TileLoads<F>& L, int nk, v16f (&acc)[F
 }
 
 // ---------------------------------------------------------------------------------------------
-// Two waves per SIMD (the forward and weight-gradient GEMMs).  A workgroup with one wave per
-// SIMD keeps one stage (64 KB) of loads in flight and a wave's loads return at a bounded rate,
+// Two waves per SIMD (every expert GEMM; the one-wave-per-SIMD loop above serves the ring
+// kernel).  A workgroup with one wave per SIMD keeps one stage (64 KB) of loads in flight and a
+// wave's loads return at a bounded rate,
 // so the loop above spends most of each stage waiting for its loads (measured: about 1.5 us per
 // 64 KB per workgroup even from L2, while two workgroups per compute unit move twice as much).
 // Here 512 threads (8 waves, two per SIMD) share the same 256 x 256 tile and its loads: wave w
