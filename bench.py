@@ -137,6 +137,41 @@ def measured_traffic(phase: str, ring: bool):
     return round(sum(table[k] for k in keys) * 1e9)
 
 
+# ----------------------------------------------------------------------------- measured peaks
+
+def measured_peaks(moe, torch, stream) -> dict:
+    """What this device reaches, next to the published peaks: the scaled MXFP8 matrix-core issue
+    rate (the library's register-only probe), an HBM copy (read + write) and an HBM fill (write
+    only) of 2 GiB, each the best of three timed runs."""
+    def best(fn, n=3):
+        t = []
+        for _ in range(n + 1):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            t.append(a.elapsed_time(b) * 1e-3)
+        return min(t[1:])  # the first is a warmup
+    need = int(-moe.moe_probe_mfma(None, 1))
+    sink = torch.empty(need // 4, dtype=torch.float32, device="cuda")
+    flop = [0.0]
+
+    def mfma():
+        flop[0] = moe.moe_probe_mfma(sink, 4000, stream)
+    t_mfma = best(mfma)
+    n = 1 << 31
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    t_copy = best(lambda: dst.copy_(src))
+    t_fill = best(lambda: dst.fill_(0))
+    del src, dst, sink
+    return {"mfma_mxfp8_tflops": round(flop[0] / t_mfma / 1e12, 1), "hbm_copy_gbps": round(2 * n / t_copy / 1e9, 1),
+            "hbm_write_gbps": round(n / t_fill / 1e9, 1),
+            "how": "register-only v_mfma_scale_f32_32x32x64_f8f6f4 loop (moe_probe_mfma); 2 GiB device copy "
+                   "(read + write bytes); 2 GiB fill; best of 3"}
+
+
 # ----------------------------------------------------------------------------- CPU baseline
 
 def host_resources() -> dict:
@@ -364,6 +399,12 @@ def main() -> int:
     roof["kernel"] = dom
     roof["timed_in"] = "timed region" if clean else "launch-order pass"
 
+    peaks = measured_peaks(moe, torch, stream)
+    log(f"[bench] measured peaks {peaks}")
+    roof["measured_peak"] = (peaks["mfma_mxfp8_tflops"] if roof["bound"] == "mfma" else
+                             peaks["hbm_copy_gbps"])
+    roof["frac_of_measured"] = round(roof["achieved"] / roof["measured_peak"], 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU baseline: oracle on a sample of {args.cpu_experts} experts")
@@ -396,6 +437,7 @@ def main() -> int:
         "phases": phases,
         "schedule": sched,
         "roofline": roof,
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -282,6 +282,16 @@ enum {
 };
 moe_status moe_set_phase_events(hipEvent_t* events, int32_t n_events);
 
+/* Measurement only (the MXFP8 roofline the layer's GEMM phases are reported against, next to
+ * the published dense peak): enqueues on `stream` one launch of register-only scaled MXFP8
+ * matrix instructions (v_mfma_scale_f32_32x32x64_f8f6f4, four waves per SIMD on every compute
+ * unit, `iters` x 4 instructions per wave) and returns its algorithmic flop count in *flop; the
+ * caller times the launch.  `sink` (device, sink_bytes) receives one float per thread; too small
+ * a sink: MOE_EWORKSPACE, with *flop set to 0 and the size needed in *sink_needed when not NULL.
+ * iters < 1: MOE_EINVAL. */
+moe_status moe_probe_mfma(float* sink, size_t sink_bytes, int32_t iters, double* flop, size_t* sink_needed,
+                          hipStream_t stream);
+
 /* Reads the device status word of `workspace` (0 = fine; else a MOE_DEV_* code) into
  * *device_code: the layer's way to report a device-side anomaly without a host sync inside the
  * layer (knowledge card, 方法/产品要点: no CPU-GPU synchronisation).  Blocking copy: call after

@@ -25,7 +25,7 @@ MOE_DEV_RING_TIMEOUT, MOE_DEV_NONFINITE_LOGIT = 1, 2
 
 # every symbol include/moe.h declares
 EXPORTS = ("moe_query", "moe_quantize_mxfp8", "moe_requant_transpose", "moe_fwd", "moe_fwd_noalloc", "moe_bwd",
-           "moe_set_phase_events", "moe_device_status", "moe_strerror")
+           "moe_set_phase_events", "moe_device_status", "moe_strerror", "moe_probe_mfma")
 MOE_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 # phases of moe_fwd / moe_bwd (include/moe.h, MOE_PH_*)
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.moe_fwd_noalloc.argtypes = [ctypes.POINTER(moe_config), P, P, P, P, P, P, P, P, P, P, SZ, P]
         L.moe_bwd.argtypes = [ctypes.POINTER(moe_config), P, P, P, P, SZ, P, P, P, P, P, P, SZ, P]
         L.moe_set_phase_events.argtypes = [P, I32]
+        L.moe_probe_mfma.argtypes = [P, ctypes.c_size_t, I32, ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_size_t), P]
         L.moe_device_status.argtypes = [P, ctypes.POINTER(I32)]
         L.moe_strerror.argtypes = [ctypes.c_int]
         L.moe_strerror.restype = ctypes.c_char_p
@@ -167,6 +169,19 @@ def moe_bwd(cfg, dy, x, w_router, saved, dx_bf16, dx_f32, dw_router, dw1, dw2, w
     _check(lib().moe_bwd(ctypes.byref(cfg), _ptr(dy), _ptr(x), _ptr(w_router), _ptr(saved),
                          _nbytes(saved, saved_bytes), _ptr(dx_bf16), _ptr(dx_f32), _ptr(dw_router), _ptr(dw1),
                          _ptr(dw2), _ptr(workspace), _nbytes(workspace, workspace_bytes), _stream(stream)), "moe_bwd")
+
+
+def moe_probe_mfma(sink, iters: int, stream=None, sink_bytes=None) -> float:
+    """Enqueue the matrix-core issue-rate probe; returns the launch's flop count (the caller times
+    it).  sink=None asks for the sink size instead: returns -(bytes needed)."""
+    flop = ctypes.c_double(0.0)
+    need = ctypes.c_size_t(0)
+    st = lib().moe_probe_mfma(_ptr(sink), 0 if sink is None else _nbytes(sink, sink_bytes), int(iters),
+                              ctypes.byref(flop), ctypes.byref(need), _stream(stream))
+    if sink is None and st == MOE_EWORKSPACE:
+        return -float(need.value)
+    _check(st, "moe_probe_mfma")
+    return flop.value
 
 
 def moe_set_phase_events(events, n_events: int) -> None:

@@ -644,6 +644,21 @@ moe_status moe_device_status(const void* workspace, int32_t* device_code) {
   return code == 0 ? MOE_OK : MOE_EDEVICE;
 }
 
+moe_status moe_probe_mfma(float* sink, size_t sink_bytes, int32_t iters, double* flop, size_t* sink_needed,
+                          hipStream_t stream) {
+  if (!flop) return MOE_EINVAL;
+  *flop = 0.0;
+  if (iters < 1) return MOE_EINVAL;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return MOE_ELAUNCH;
+  const size_t need = probe_mfma_sink_bytes(cus);
+  if (sink_needed) *sink_needed = need;
+  if (!sink || sink_bytes < need) return MOE_EWORKSPACE;
+  return launch_probe_mfma(sink, cus, iters, flop, stream) == hipSuccess ? MOE_OK : MOE_ELAUNCH;
+}
+
 const char* moe_strerror(moe_status s) {
   switch (s) {
     case MOE_OK: return "ok";

@@ -97,6 +97,10 @@ hipError_t launch_permute_rows(const SchedView& s, const uint8_t* xq, const uint
 hipError_t launch_swiglu_quant(const float* g, const float* u, int RS, int I, uint8_t* hq, uint8_t* hs, hipStream_t);
 hipError_t launch_unpermute_rows(const SchedView& s, const float* yrows, int RS, int d, float* yslot, hipStream_t);
 
+// Measurement: the matrix core's MXFP8 issue rate (register operands only).
+size_t probe_mfma_sink_bytes(int cus);
+hipError_t launch_probe_mfma(float* sink, int cus, int iters, double* flop, hipStream_t);
+
 // MXFP8 quantisation along the contiguous axis of a [rows, cols] bf16 (src_f32 = 0) or
 // float32 (src_f32 = 1) matrix.
 hipError_t launch_quant_rows(const void* src, int src_f32, int64_t rows, int64_t cols, uint8_t* q,

@@ -185,3 +185,9 @@ def test_strerror_covers_every_status():
     for s in range(7):
         assert moe.moe_strerror(s) and moe.moe_strerror(s) != "unknown status"
     assert moe.moe_strerror(99) == "unknown status"
+
+
+def test_mfma_probe_rejects_bad_arguments_without_launching():
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_probe_mfma(1 << 20, 0, stream=0, sink_bytes=1 << 30)
+    assert ei.value.status == moe.MOE_EINVAL
