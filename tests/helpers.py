@@ -27,7 +27,10 @@ K1_SHARED = moe_inputs.LayerConfig("k1_shared", T=130, d=384, E=6, k=1, inter=12
                                    n_shared=1)
 # the API's routing limits: 512 experts, top-16 (most experts see a few rows, many none)
 MAX_ROUTE = moe_inputs.LayerConfig("max_route", T=70, d=128, E=512, k=16, inter=128, score="softmax", seed=13)
-CASES = [moe_inputs.CONFIGS["tiny"], MID, MID_SIG, RAGGED, EMPTY, K_EQ_E, K1_SHARED, MAX_ROUTE]
+# one token (two routed rows and a shared row; every other expert empty)
+ONE_TOKEN = moe_inputs.LayerConfig("one_token", T=1, d=256, E=8, k=2, inter=128, score="sigmoid", seed=14,
+                                   n_shared=1)
+CASES = [moe_inputs.CONFIGS["tiny"], MID, MID_SIG, RAGGED, EMPTY, K_EQ_E, K1_SHARED, MAX_ROUTE, ONE_TOKEN]
 
 
 def log(*a):

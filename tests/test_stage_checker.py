@@ -11,6 +11,8 @@ CASES = [
     moe_inputs.LayerConfig("small", T=40, d=128, E=4, k=2, inter=128, score="softmax", seed=21, backward=True),
     moe_inputs.LayerConfig("small_shared", T=33, d=256, E=6, k=2, inter=128, score="sigmoid", seed=22,
                            n_shared=1, zipf_s=1.1, zipf_lam=1.0, backward=True),
+    moe_inputs.LayerConfig("one_token", T=1, d=256, E=8, k=2, inter=128, score="sigmoid", seed=23, n_shared=1,
+                           backward=True),
 ]
 
 
@@ -50,6 +52,7 @@ def test_checker_rejects_planted_mistakes(fake):
     cfg, inp, ws, layer = fake
     e = int(np.argmax(layer.saved_tensor("counts").numpy()[:cfg.E]))
     lo = int(layer.saved_tensor("offsets")[e])
+    t1, t2 = min(1, cfg.T - 1), min(2, cfg.T - 1)
     plants = {
         # W1t requantised along the wrong axis (blocks along d instead of 2I): codes differ
         "w1t axis": lambda L: _swap(L.saved_tensor("w1t")[e], L.w1q[e].T.contiguous()),
@@ -64,9 +67,9 @@ def test_checker_rejects_planted_mistakes(fake):
         # dW1 of the expert transposed wrong: gate and up halves swapped
         "dw1 halves": lambda L: _swap(L.dw1[e], L.dw1[e].roll(cfg.inter, dims=0)),
         # dx missing the router term of one token
-        "dx": lambda L: _swap(L.dx32[1], L.dx32[1] * 0.9),
+        "dx": lambda L: _swap(L.dx32[t1], L.dx32[t1] * 0.9),
         # the combine weights of one token swapped
-        "w": lambda L: _swap(L.saved_tensor("w")[2], L.saved_tensor("w")[2].flip(0)),
+        "w": lambda L: _swap(L.saved_tensor("w")[t2], L.saved_tensor("w")[t2].flip(0)),
     }
     for name, plant in plants.items():
         _expect_failure(cfg, inp, ws, layer, plant)
