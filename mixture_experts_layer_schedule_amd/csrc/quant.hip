@@ -200,50 +200,99 @@ MOE_DEV int find_tile(const int32_t* start, int n, int tile) {
   return lo;
 }
 
-// Token-axis requantisation: 64 tokens of one expert x 64 columns per workgroup.
+// Token-axis requantisation: 128 tokens of one expert x 128 columns per workgroup, the
+// 128 x 128 transposed scheme above with the rows gathered through the schedule.  Token x of
+// the tile is the expert's row tl + x (zero past its rows: the segment's padding); for X and w*dY
+// the source row is that row's token, for H and [dG dU] the permuted row itself.  Loads: 8 lanes
+// cover a whole 128-byte line of a source row; stores: each output row (a column of the source)
+// gets 128 contiguous token codes from two lanes.  w*dY multiplies the exactly dequantised value
+// by the row's combine weight before the requantisation.
 __global__ __launch_bounds__(256) void k_token_requant(TokArgs p) {
-  __shared__ float tile[TS * TP];
+  __shared__ __align__(16) uint8_t ct[RT * RPITCH];  // ct[c][x]: code of token x, column c
+  __shared__ __align__(16) uint8_t sct[4][RT];       // sct[c / 32][x]: its scale byte
+  __shared__ float wt[RT];                            // combine weight of token x (w*dY)
   const SchedView& s = p.s;
-  const int tile_id = blockIdx.y;
-  if (tile_id >= p.tile64[s.n_exp]) return;
-  const int e = find_tile(p.tile64, s.n_exp, tile_id);
-  const int tl = (tile_id - p.tile64[e]) * TS;   // first local token of the tile
+  const int t128 = blockIdx.y;
+  if (2 * t128 >= p.tile64[s.n_exp]) return;
+  const int e = find_tile(p.tile64, s.n_exp, 2 * t128);  // segments are 128-padded: even 64-tiles
+  const int tl = (2 * t128 - p.tile64[e]) * TS;            // first local token of the tile
   const int r0 = s.offsets[e];
   const int cnt = s.offsets[e + 1] - r0;
-  const int c0 = blockIdx.x * TS;
+  const int64_t c0 = (int64_t)blockIdx.x * RT;
   const int t = threadIdx.x;
   {
-    const int x = t >> 2, part = t & 3;
-    const int col = c0 + 16 * part;
-    float v[16];
-    if (tl + x < cnt) {
-      const int r = r0 + tl + x;
-      int64_t srow;
-      if (p.src == TOK_X || p.src == TOK_DYW) {
-        srow = r < s.R ? s.perm[r] / s.k : (r - s.R) % s.T;
+    const int rg = t >> 3, cg = t & 7;
+    v4i w[4];
+    uint32_t sb = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int x = 4 * rg + j;
+      if (tl + x < cnt) {
+        const int r = r0 + tl + x;
+        int64_t srow;
+        if (p.src == TOK_X || p.src == TOK_DYW) srow = r < s.R ? s.perm[r] / s.k : (r - s.R) % s.T;
+        else srow = r;
+        w[j] = *(const v4i*)(p.q + srow * p.cols + c0 + 16 * cg);
+        sb |= (uint32_t)p.qs[srow * (p.cols / 32) + (c0 + 16 * cg) / 32] << (8 * j);
       } else {
-        srow = r;
+        w[j] = (v4i){0, 0, 0, 0};
       }
-      v4i codes = *(const v4i*)(p.q + srow * p.cols + col);
-      uint32_t sb = p.qs[srow * (p.cols / 32) + col / 32];
-      dq16(codes, sb, v);
-      if (p.src == TOK_DYW) {
-        float wr = r < s.R ? p.w[s.perm[r]] : 1.0f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] *= wr;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = 0.0f;
     }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) tile[(16 * part + j) * TP + x] = v[j];
+    for (int m = 0; m < 16; ++m) {
+      const int sh = 8 * (m & 3);
+      const uint32_t col4 = (((uint32_t)w[0][m >> 2] >> sh) & 0xFFu) | ((((uint32_t)w[1][m >> 2] >> sh) & 0xFFu) << 8) |
+                            ((((uint32_t)w[2][m >> 2] >> sh) & 0xFFu) << 16) | ((((uint32_t)w[3][m >> 2] >> sh) & 0xFFu) << 24);
+      *(uint32_t*)(ct + (16 * cg + m) * RPITCH + 4 * rg) = col4;
+    }
+    if ((cg & 1) == 0) *(uint32_t*)(&sct[cg >> 1][4 * rg]) = sb;
+    if (t < RT) {
+      const int r = r0 + tl + t;
+      wt[t] = (p.src == TOK_DYW && tl + t < cnt && r < s.R) ? p.w[s.perm[r]] : 1.0f;
+    }
   }
   __syncthreads();
-  const int c = t >> 2, part = t & 3;
-  const int64_t o = p.tok_off[e] + tl;
-  quant_tile_out(tile, p.out + (int64_t)(c0 + c) * p.ld + o, p.outs + (int64_t)(c0 + c) * (p.ld / 32) + o / 32,
-                 part);
+  const int c = t >> 1, half = t & 1;
+  const uint32_t* crow = (const uint32_t*)(ct + c * RPITCH + 64 * half);
+  const uint32_t* srow = (const uint32_t*)(&sct[c >> 5][64 * half]);
+  const int64_t o = p.tok_off[e] + tl + 64 * half;  // output token column
+  uint8_t* dst = p.out + (c0 + c) * p.ld + o;
+  uint8_t* sdst = p.outs + (c0 + c) * (p.ld / 32) + o / 32;
+  const bool dyw = p.src == TOK_DYW;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    float v[32];
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {  // 4 codes of 4 consecutive tokens per word
+      const uint32_t codes = crow[8 * blk + k];
+      const uint32_t sc4 = srow[8 * blk + k];
+      const v2f p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, false);
+      const v2f p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, true);
+      v[4 * k + 0] = p0[0] * e8m0_scale(sc4 & 0xFFu);
+      v[4 * k + 1] = p0[1] * e8m0_scale((sc4 >> 8) & 0xFFu);
+      v[4 * k + 2] = p1[0] * e8m0_scale((sc4 >> 16) & 0xFFu);
+      v[4 * k + 3] = p1[1] * e8m0_scale(sc4 >> 24);
+      if (dyw) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) v[4 * k + x] *= wt[64 * half + 32 * blk + 4 * k + x];
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x) m = fmaxf(m, fabsf(v[4 * k + x]));
+    }
+    const uint32_t byte = e8m0_from_amax(m);
+    const float inv = e8m0_inv_scale(byte);
+    v4i o0, o1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      o0[k] = (int)pack4_e4m3(v[4 * k] * inv, v[4 * k + 1] * inv, v[4 * k + 2] * inv, v[4 * k + 3] * inv);
+      o1[k] = (int)pack4_e4m3(v[16 + 4 * k] * inv, v[16 + 4 * k + 1] * inv, v[16 + 4 * k + 2] * inv,
+                              v[16 + 4 * k + 3] * inv);
+    }
+    ((v4i*)dst)[2 * blk] = o0;
+    ((v4i*)dst)[2 * blk + 1] = o1;
+    sdst[blk] = (uint8_t)byte;
+  }
 }
 
 }  // namespace
@@ -275,7 +324,9 @@ hipError_t launch_requant_t(const uint8_t* q, const uint8_t* s, int64_t batch, i
 }
 
 hipError_t launch_token_requant(const TokArgs& a, int tiles_bound, hipStream_t stream) {
-  dim3 grid((unsigned)(a.cols / TS), (unsigned)tiles_bound);
+  if (a.cols % RT) return hipErrorInvalidValue;
+  // tiles_bound counts 64-token tiles; the kernel takes 128 tokens per workgroup
+  dim3 grid((unsigned)(a.cols / RT), (unsigned)((tiles_bound + 1) / 2));
   hipLaunchKernelGGL(k_token_requant, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
