@@ -266,6 +266,10 @@ def main() -> int:
                     help="time moe_fwd alone (MOE_F_FORWARD_ONLY: no state saved for a backward pass)")
     ap.add_argument("--unfused", action="store_true",
                     help="the unfused forward baseline (MOE_F_UNFUSED; implies --forward-only)")
+    ap.add_argument("--chunk-rows", type=int, default=0,
+                    help="rows per GEMM row tile (moe_config.chunk_rows); 0: tuned per workload")
+    ap.add_argument("--no-tune", action="store_true",
+                    help="skip the per-workload tuning (chunk_rows 256, backward branch on a second stream)")
     args = ap.parse_args()
     if args.unfused:
         args.forward_only = True
@@ -295,6 +299,21 @@ def main() -> int:
     log(f"[bench] setup {time.time() - t0:.1f} s")
 
     stream = torch.cuda.current_stream()
+    # per-workload tuning before anything is timed: every candidate gives the same bits
+    tuning = None
+    if args.chunk_rows:
+        layer.cfg.chunk_rows = args.chunk_rows
+    elif not args.no_tune:
+        from mixture_experts_layer_schedule_amd import tune as tuner
+        t_tune = time.time()
+        res = tuner.tune(layer, backward=not fwd_only, steps=3, warmup=1, stream=stream)
+        tuning = {"chosen": res.best.label(), "ms_per_step": res.table(),
+                  "how": "each candidate timed for 3 steps after 1 warm-up step on the same inputs; "
+                         "the default (first) stays unless beaten by more than 1 %"}
+        log(f"[bench] tuned in {time.time() - t_tune:.1f} s: {res.best.label()} "
+            f"({', '.join(f'{k} {v:.2f}' for k, v in list(res.table().items())[:4])} ms)")
+    knobs = {"chunk_rows": int(layer.cfg.chunk_rows) or 256,
+             "serial_bwd": bool(layer.cfg.flags & moe.MOE_F_SERIAL_BWD)}
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -341,7 +360,7 @@ def main() -> int:
     # the timed region: the library's default schedule (backward branch on a second stream)
     ms, phase_ms_timed = timed(args.steps)
     log(f"[bench] {args.steps} steps, {ms:.3f} ms/step")
-    if fwd_only:  # the forward runs on one stream: its phase marks come from the timed region
+    if fwd_only or knobs["serial_bwd"]:  # one stream: the phase marks come from the timed region
         ms_serial, phase_ms = ms, phase_ms_timed
     else:
         # per-phase breakdown: the same step with every kernel in launch order on one stream
@@ -428,7 +447,8 @@ def main() -> int:
                                 f"I={cfg.inter} {cfg.score}, seed {cfg.seed}"),
                    "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "inter": cfg.inter, "score": cfg.score,
                    "n_shared": cfg.n_shared, "seed": cfg.seed, "parallelism": "single GPU",
-                   "path": "unfused" if args.unfused else "fused"},
+                   "path": "unfused" if args.unfused else "fused", **knobs},
+        "tuning": tuning,
         "tflops": round(tflops, 2),
         "mfma_frac_layer": round(flops_gemm / (ms * 1e-3) / MXFP8_PEAK, 4),
         "mfma_frac_gemms": round(flops_gemm / (gemm_ms * 1e-3) / MXFP8_PEAK, 4),

@@ -64,8 +64,12 @@ typedef enum moe_score_fn {
  * n_shared)) below 2^24 (several kernels address an operand with 32-bit byte offsets).
  * The tuning fields are the pages' per-workload knobs (buffer capacity, minibatch and number of
  * communication SMs: article "Cursor 為 Composer 改造 MoE 訓練…", section "2.37 倍同 1.41 倍係兩份
- * 成績"); they only act on the ring dispatch (MOE_F_RING_DISPATCH) and must be 0 otherwise.  0
- * picks a default.  They never change results. */
+ * 成績").  chunk_rows, the rows of one GEMM row tile (the unit of work the grouped GEMMs and the
+ * ring hand out), acts on every path: smaller tiles give more work items per GEMM for few rows
+ * per expert, at the cost of streaming each weight slice once more per extra tile.  ring_rows and
+ * producer_wgs act on the ring dispatch (MOE_F_RING_DISPATCH) only and must be 0 otherwise.  0
+ * picks a default.  They never change results.  moe_bwd must see the chunk_rows of the moe_fwd
+ * whose saved schedule it reuses (the saved row-tile table is built for it). */
 typedef struct moe_config {
   int32_t T;          /* tokens */
   int32_t d;          /* hidden size */
@@ -75,7 +79,8 @@ typedef struct moe_config {
   int32_t n_shared;   /* always-on shared experts (weight 1), stored after the E routed ones */
   int32_t score_fn;   /* moe_score_fn */
   int32_t ring_rows;  /* ring token buffer capacity in rows (0 = default; multiple of 256) */
-  int32_t chunk_rows; /* rows per ring slot (0 = default; only 256 is supported) */
+  int32_t chunk_rows; /* rows per GEMM row tile at most (0 = 256; a multiple of 32 up to 256;
+                         the ring dispatch takes 256 only) */
   int32_t producer_wgs; /* gather (producer) workgroups of the persistent dispatch kernel (0 = default, max 128) */
   uint32_t flags;     /* MOE_F_* */
 } moe_config;
@@ -135,7 +140,7 @@ typedef struct moe_saved_layout {
   size_t offsets;    /* int32 [NX + 1]     first permuted row of each expert */
   size_t poffsets;   /* int32 [NX + 1]     offsets with every count rounded up to 32 */
   size_t tok_off;    /* int64 [NX + 1]     offsets with every count rounded up to 128 */
-  size_t tile_start; /* int32 [NX + 1]     first row tile of each expert (ceil(count / 256) each) */
+  size_t tile_start; /* int32 [NX + 1]     first row tile of each expert (ceil(count / chunk_rows) each) */
   size_t tile64;     /* int32 [NX + 1]     first 64-row tile of each 128-padded segment */
   size_t perm;       /* int32 [R]          slot id t*k + j of each routed permuted row */
   size_t pos;        /* int32 [T, k]       permuted row of slot (t, j) */

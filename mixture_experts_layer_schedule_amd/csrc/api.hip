@@ -16,6 +16,7 @@ size_t up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 struct Dims {
   int64_t T, d, E, k, I, S, NX, R, RS, nblk, ld_tok, tiles_bound, tile64_bound;
   int64_t nslots, producers;
+  int64_t tile_rows;  // rows per GEMM row tile at most (chunk_rows)
   bool unfused;
 };
 
@@ -32,7 +33,8 @@ Dims dims(const moe_config& c) {
   m.RS = m.R + m.S * m.T;
   m.nblk = (m.T + kSchedBlockTokens - 1) / kSchedBlockTokens;
   m.ld_tok = (int64_t)up((size_t)(m.RS + 127 * m.NX), 128);
-  m.tiles_bound = m.RS / 256 + m.NX + 1;  // sum over experts of ceil(count / 256)
+  m.tile_rows = c.chunk_rows ? c.chunk_rows : kChunkRows;
+  m.tiles_bound = m.RS / m.tile_rows + m.NX + 1;  // sum over experts of ceil(count / tile_rows)
   m.tile64_bound = m.ld_tok / 64;
   // the ring buffer exists only for the ring dispatch
   const int64_t ring_rows = !(c.flags & MOE_F_RING_DISPATCH) ? 0 : c.ring_rows ? c.ring_rows : kDefaultRingRows;
@@ -56,10 +58,12 @@ moe_status check_config(const moe_config* c) {
   if ((c->flags & MOE_F_DIRECT_GATHER) && (c->flags & MOE_F_RING_DISPATCH)) return MOE_EINVAL;
   if (c->flags & MOE_F_RING_DISPATCH) return MOE_EINVAL;  // disabled: see the ring kernel's header
   // the tuning knobs only act on the ring dispatch
-  if (!(c->flags & MOE_F_RING_DISPATCH) && (c->ring_rows || c->chunk_rows || c->producer_wgs)) return MOE_EINVAL;
+  if (!(c->flags & MOE_F_RING_DISPATCH) && (c->ring_rows || c->producer_wgs)) return MOE_EINVAL;
   if (c->ring_rows < 0 || c->producer_wgs < 0 || c->producer_wgs > 128) return MOE_ESHAPE;
   if (c->ring_rows && (c->ring_rows < kChunkRows || c->ring_rows % kChunkRows)) return MOE_ESHAPE;
-  if (c->chunk_rows != 0 && c->chunk_rows != kChunkRows) return MOE_ESHAPE;
+  // rows per GEMM row tile: every path; the ring's slots hold whole 256-row tiles
+  if (c->chunk_rows < 0 || c->chunk_rows > kChunkRows || c->chunk_rows % 32) return MOE_ESHAPE;
+  if ((c->flags & MOE_F_RING_DISPATCH) && c->chunk_rows && c->chunk_rows != kChunkRows) return MOE_ESHAPE;
   const int64_t RS = (int64_t)c->T * c->k + (int64_t)c->n_shared * c->T;
   if (RS >= (1ll << 30)) return MOE_ESHAPE;
   // operands addressed with 32-bit byte offsets from one base: the gathered activations
@@ -289,6 +293,7 @@ moe_status forward_impl(const moe_config* cfg, const Dims& m, const moe_saved_la
   sb.E = (int)m.E;
   sb.k = (int)m.k;
   sb.S = (int)m.S;
+  sb.tile_rows = (int)m.tile_rows;
   mark(stream, MOE_PH_TOPK);
   MOE_TRY(launch_schedule(sb, stream));
   mark(stream, MOE_PH_SCHEDULE);

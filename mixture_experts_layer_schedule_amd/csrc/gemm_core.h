@@ -89,10 +89,11 @@ MOE_DEV int tile_expert(const int32_t* tile_start, int n_exp, int tile) {
 }
 
 // Rows [r0, r0 + rows) of expert e covered by its m-th row tile.  An expert with c rows has
-// ceil(c / 256) tiles; the rows are split evenly between them in multiples of 32, so a 300-row
-// expert runs as two 160-row tiles rather than 256 + 44.  rows <= 0 only for experts of more
-// than 2048 rows, whose last tile can come out empty.  (A wider tile would need more than the
-// 256 accumulator registers per lane.)
+// ceil(c / tile rows) tiles (tile rows: the configured chunk, 256 by default); the rows are split
+// evenly between them in multiples of 32, so a 300-row expert runs as two 160-row tiles rather
+// than 256 + 44.  The rounding to 32 could in principle leave the last tile empty (rows <= 0;
+// no expert below 70,000 rows does, for any tile height up to 256), and every kernel skips such a
+// tile.  (A wider tile would need more than the 256 accumulator registers per lane.)
 struct RowTile {
   int e, r0, rows;
   int m, nm;  // index of the tile among the expert's nm row tiles

@@ -12,7 +12,7 @@ constexpr int kSchedBlockTokens = 64;
 struct SchedView {
   const int32_t* perm;        // [R] slot id t*k + j of each routed permuted row
   const int32_t* offsets;     // [n_exp + 1] first permuted row of each expert
-  const int32_t* tile_start;  // [n_exp + 1] first row tile of each expert (ceil(count / 256) each)
+  const int32_t* tile_start;  // [n_exp + 1] first row tile of each expert (ceil(count / tile rows) each)
   int n_exp;                  // routed + shared experts
   int R;                      // routed rows T * k (shared rows follow)
   int T, k, S;
@@ -139,11 +139,12 @@ struct SchedBuild {
   int32_t* offsets;     // [n_exp + 1]
   int32_t* poffsets;    // [n_exp + 1] padded to 32
   int64_t* tok_off;     // [n_exp + 1] padded to 128 (weight-gradient operands)
-  int32_t* tile_start;  // [n_exp + 1] row tiles of up to 256 rows
+  int32_t* tile_start;  // [n_exp + 1] row tiles of up to tile_rows rows
   int32_t* tile64;      // [n_exp + 1] 64-token tiles over the 128-padded segments
   int32_t* perm;        // [R]
   int32_t* pos;         // [T, k]
   int T, E, k, S;
+  int tile_rows;        // rows per GEMM row tile at most (32 .. 256, a multiple of 32)
 };
 hipError_t launch_schedule(const SchedBuild&, hipStream_t);
 

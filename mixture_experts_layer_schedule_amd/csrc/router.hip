@@ -186,8 +186,8 @@ __global__ __launch_bounds__(64) void k_sched_colscan(SchedBuild p, int nblk) {
 }
 
 // One workgroup: exclusive prefixes over the experts (routed, then shared with T rows each) of
-// the counts, the counts rounded up to 32 and to 128, the 256-row tiles and the 64-token tiles,
-// by wavefront scans within waves and one scan of the wave totals.
+// the counts, the counts rounded up to 32 and to 128, the GEMM row tiles (of up to tile_rows
+// rows) and the 64-token tiles, by wavefront scans within waves and one scan of the wave totals.
 __global__ __launch_bounds__(1024) void k_sched_offsets(SchedBuild p) {
   __shared__ int64_t wsum[16][5];
   const int n_exp = p.E + p.S;
@@ -195,7 +195,8 @@ __global__ __launch_bounds__(1024) void k_sched_offsets(SchedBuild p) {
   int c = 0;
   if (i < p.E) c = p.counts[i];
   else if (i < n_exp) c = p.T;
-  int64_t v[5] = {c, (c + 31) / 32 * 32, (c + 127) / 128 * 128, (c + 255) / 256, (c + 127) / 128 * 2};
+  int64_t v[5] = {c, (c + 31) / 32 * 32, (c + 127) / 128 * 128, (c + p.tile_rows - 1) / p.tile_rows,
+                  (c + 127) / 128 * 2};
   int64_t incl[5];
 #pragma unroll
   for (int q = 0; q < 5; ++q) {

@@ -218,6 +218,67 @@ def test_serial_and_concurrent_backward_identical(pair):
         assert torch.equal(a, b), name
 
 
+@pytest.mark.parametrize("rows", [32, 96, 128])
+def test_row_tile_height_changes_no_bit(pair, rows):
+    """chunk_rows (rows per GEMM row tile, the tuning knob of the direct path) changes the work
+    items only: the row-tile table is ceil(count / rows) per expert, and every output, gradient
+    and saved or workspace stage result is bitwise that of the default 256-row tiles."""
+    cfg, inp, fw, bw, layer = pair
+    import torch
+    names = ("y", "y32", "dx", "dx32", "dw1", "dw2", "dw_r")
+    saved = ("g", "u", "hq", "hs", "yslot")
+    work = ("dguq", "dgus", "dxslot")
+    layer.cfg.chunk_rows = 0
+    layer.forward()
+    layer.backward()
+    torch.cuda.synchronize()
+    ref = {n: getattr(layer, n).clone() for n in names}
+    ref.update({n: layer.saved_tensor(n).clone() for n in saved})
+    ref.update({n: layer.workspace_tensor(n).clone() for n in work})
+    try:
+        layer.cfg.chunk_rows = rows
+        for n in names:
+            getattr(layer, n).zero_()
+        layer.forward()
+        layer.backward()
+        torch.cuda.synchronize()
+        counts = to_np(layer.saved_tensor("counts")).astype(np.int64)
+        tiles = np.concatenate([[0], np.cumsum(-(-counts // rows))])
+        assert np.array_equal(to_np(layer.saved_tensor("tile_start")), tiles)
+        got = {n: getattr(layer, n) for n in names}
+        got.update({n: layer.saved_tensor(n) for n in saved})
+        got.update({n: layer.workspace_tensor(n) for n in work})
+        for n in ref:
+            assert torch.equal(ref[n], got[n]), (cfg.name, rows, n)
+    finally:
+        layer.cfg.chunk_rows = 0
+
+
+def test_tuner_picks_a_candidate_and_keeps_the_bits():
+    """The per-workload tuner times its candidates on a layer and leaves the fastest in its
+    configuration; the tuned layer computes the default layer's bits."""
+    import torch
+    import mixture_experts_layer_schedule_amd as moe
+    from mixture_experts_layer_schedule_amd import tune
+    cfg = moe_inputs.CONFIGS["tiny"].with_(backward=True)
+    layer = gpu_layer(cfg, True)
+    ref = [t.clone() for t in (layer.y32, layer.dx32, layer.dw1, layer.dw2, layer.dw_r)]
+    res = tune.tune(layer, backward=True, steps=1, warmup=1)
+    cands = tune.candidates(layer.T, layer.E, layer.k, layer.S, True)
+    assert res.best in cands and set(res.ms) == set(cands)
+    log("tuner: " + ", ".join(f"{k} {v:.3f}" for k, v in res.table().items()))
+    assert layer.cfg.chunk_rows == res.best.chunk_rows
+    assert bool(layer.cfg.flags & moe.MOE_F_SERIAL_BWD) == res.best.serial_bwd
+    for t in (layer.y32, layer.dx32, layer.dw1, layer.dw2, layer.dw_r):
+        t.zero_()
+    layer.forward()
+    layer.backward()
+    torch.cuda.synchronize()
+    for name, a, b in zip(("y", "dx", "dW1", "dW2", "dW_r"), ref,
+                          (layer.y32, layer.dx32, layer.dw1, layer.dw2, layer.dw_r)):
+        assert torch.equal(a, b), name
+
+
 def test_nonfinite_logits_route_to_valid_experts():
     """A token whose router logits are all NaN (a NaN in its x row) still selects k distinct valid
     experts (NaN ranks as -inf, ties to the lower index: experts 0..k-1), the schedule stays a

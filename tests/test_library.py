@@ -39,6 +39,15 @@ def test_header_structs_match_the_binding():
     assert fields == [f for f, _ in moe.moe_config._fields_]
 
 
+@pytest.mark.parametrize("rows", [32, 64, 96, 128, 192, 256])
+def test_row_tile_heights_are_accepted_on_the_direct_path(rows):
+    """chunk_rows (rows per GEMM row tile) is a tuning knob of every path and leaves the buffer
+    layouts unchanged."""
+    ws0, sl0 = moe.moe_query(moe.make_config(4096, 256, 8, 2, 128))
+    ws, sl = moe.moe_query(moe.make_config(4096, 256, 8, 2, 128, chunk_rows=rows))
+    assert ws == ws0 and sl.total == sl0.total
+
+
 def test_query_layout_is_aligned_and_ordered():
     cfg = moe.make_config(256, 256, 8, 2, 128)
     ws, sl, wl = moe.moe_query(cfg, with_workspace_layout=True)
@@ -69,9 +78,12 @@ def test_forward_only_layout_drops_transposed_weights():
     (dict(n_shared=2), moe.MOE_ESHAPE),
     (dict(score_fn=7), moe.MOE_EINVAL),
     (dict(T=0), moe.MOE_ESHAPE),
-    (dict(ring_rows=256), moe.MOE_EINVAL),   # tuning knobs only act on the ring dispatch
-    (dict(chunk_rows=256), moe.MOE_EINVAL),
+    (dict(ring_rows=256), moe.MOE_EINVAL),   # ring capacity and producers act on the ring dispatch only
     (dict(producer_wgs=8), moe.MOE_EINVAL),
+    (dict(chunk_rows=100), moe.MOE_ESHAPE),  # row tiles: multiples of 32 ...
+    (dict(chunk_rows=16), moe.MOE_ESHAPE),
+    (dict(chunk_rows=288), moe.MOE_ESHAPE),  # ... up to 256
+    (dict(chunk_rows=-32), moe.MOE_ESHAPE),
     (dict(flags=2), moe.MOE_EINVAL),         # ring dispatch is disabled
     (dict(flags=3), moe.MOE_EINVAL),         # direct gather and ring dispatch together
     (dict(flags=64), moe.MOE_EINVAL),        # unknown flag
