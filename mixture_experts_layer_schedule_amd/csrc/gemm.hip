@@ -301,7 +301,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_wgrad(WgradArgs p) {
   const int MT = p.M / (32 * kWgradF), NT = (p.N + TN - 1) / TN;
   int item;
   if (!xcd_item(p.n_exp * MT * NT, &item)) return;
-  const int nt = item % NT, mt = (item / NT) % MT, e = item / (NT * MT);
+  // Items of one expert in blocks of NB column tiles, row tiles within a block: the items in
+  // flight on an XCD (one contiguous item range per XCD) share the block's NB B tiles, which
+  // stay in its L2 while the row tiles' A tiles stream past once per block.  With every column
+  // tile in one block (NT <= 16) this is row-tile-major, column tiles fastest.
+  const int NB = NT <= 16 ? NT : (NT + 1) / 2;
+  const int e = item / (NT * MT), j = item - e * NT * MT;
+  const int nb0 = (j / (MT * NB)) * NB, nbs = min(NB, NT - nb0);
+  const int rr = j - nb0 * MT;
+  const int mt = rr / nbs, nt = nb0 + rr % nbs;
   const int64_t k0 = p.tok_off[e];
   const int K = (int)(p.tok_off[e + 1] - k0);  // multiple of 128
   const int64_t ld = p.ld;                      // token stride of At / Bt rows
