@@ -16,54 +16,79 @@ namespace {
 // L = x W_r^T on v_mfma_f32_32x32x16_bf16 (lane l = i + 32h holds row i, 8 K values; result
 // layout as for every 32x32 MFMA).  Four MFMA steps cover 64 K values; lane half h takes the
 // 32 consecutive values [32h, 32h + 32) of that span (8 per step), which only reorders the
-// float32 accumulation, identically on every run.  One wave computes 32 tokens x 32 experts.
+// float32 accumulation, identically on every run.
+//
+// A workgroup computes a 64-token x 64-expert tile: each of its 4 waves takes a quarter of the
+// 64-value K steps for all four 32 x 32 fragments (2 token x 2 expert fragments, so every
+// operand row it loads feeds two fragments), and the quarters are added in LDS in a fixed order
+// (quarter 0 + 1 + 2 + 3).  Operand rows past T or E are clamped copies whose results are not
+// stored.
 
 __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
                                                        const float* __restrict__ bias, float* __restrict__ L, int T,
                                                        int d, int E) {
+  __shared__ float part[4][4][16][64];  // [quarter][fragment][register][lane]
   const int wave = threadIdx.x >> 6, l = lane_id(), i = l & 31, h = l >> 5;
-  const int t0 = blockIdx.x * 64 + (wave >> 1) * 32;
-  const int e0 = blockIdx.y * 64 + (wave & 1) * 32;
-  const int trow = min(t0 + i, T - 1);
-  const int erow = e0 + i;
-  const bool evalid = erow < E;
-  const uint16_t* pa = x + (size_t)trow * d + 32 * h;
-  const uint16_t* pb = wr + (size_t)min(erow, E - 1) * d + 32 * h;
-  v16f acc;
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  const uint16_t* pa[2];
+  const uint16_t* pb[2];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-  // The operands of step k0 + 64 are loaded before the matrix instructions of step k0, so each
+  for (int f = 0; f < 2; ++f) {
+    pa[f] = x + (size_t)min(t0 + 32 * f + i, T - 1) * d + 32 * h;
+    pb[f] = wr + (size_t)min(e0 + 32 * f + i, E - 1) * d + 32 * h;
+  }
+  const int nsteps = d / 64, s0 = wave * nsteps / 4, s1 = (wave + 1) * nsteps / 4;
+  v16f acc[2][2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[f][g][v] = 0.0f;
+  // The operands of step k + 1 are loaded before the matrix instructions of step k, so each
   // step's load latency overlaps the previous step's products (the summation order is unchanged).
-  v8bf a[4], b[4], na[4], nb[4];
-  auto load = [&](int k0, v8bf (&ra)[4], v8bf (&rb)[4]) {
+  v8bf a[2][4], b[2][4], na[2][4], nb[2][4];
+  auto load = [&](int k0, v8bf (&ra)[2][4], v8bf (&rb)[2][4]) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      ra[s] = *(const v8bf*)(pa + k0 + 8 * s);
-      rb[s] = *(const v8bf*)(pb + k0 + 8 * s);
-    }
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        ra[f][s] = *(const v8bf*)(pa[f] + k0 + 8 * s);
+        rb[f][s] = *(const v8bf*)(pb[f] + k0 + 8 * s);
+      }
   };
-  load(0, a, b);
-  for (int k0 = 0; k0 < d; k0 += 64) {
-    if (k0 + 64 < d) load(k0 + 64, na, nb);
-    if (!evalid) {
+  if (s0 < s1) load(64 * s0, a, b);
+  for (int st = s0; st < s1; ++st) {
+    if (st + 1 < s1) load(64 * (st + 1), na, nb);
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) b[s][j] = (__bf16)0.0f;
-    }
+      for (int f = 0; f < 2; ++f)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b[s], acc, 0, 0, 0);
+        for (int g = 0; g < 2; ++g) acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[f][s], b[g][s], acc[f][g], 0, 0, 0);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      a[s] = na[s];
-      b[s] = nb[s];
-    }
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        a[f][s] = na[f][s];
+        b[f][s] = nb[f][s];
+      }
   }
 #pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) part[wave][2 * f + g][v][l] = acc[f][g][v];
+  __syncthreads();
+  // wave w finishes fragment w: token fragment w / 2, expert fragment w % 2
+  const int f = wave >> 1, g = wave & 1;
+  const int e = e0 + 32 * g + i;
+#pragma unroll
   for (int v = 0; v < 16; ++v) {
-    int t = t0 + 8 * (v >> 2) + 4 * h + (v & 3);
-    int e = e0 + i;
-    if (t < T && e < E) L[(size_t)t * E + e] = acc[v] + (bias ? bias[e] : 0.0f);
+    const int t = t0 + 32 * f + 8 * (v >> 2) + 4 * h + (v & 3);
+    const float sum = ((part[0][wave][v][l] + part[1][wave][v][l]) + part[2][wave][v][l]) + part[3][wave][v][l];
+    if (t < T && e < E) L[(size_t)t * E + e] = sum + (bias ? bias[e] : 0.0f);
   }
 }
 
