@@ -268,6 +268,9 @@ def main() -> int:
                     help="the unfused forward baseline (MOE_F_UNFUSED; implies --forward-only)")
     ap.add_argument("--chunk-rows", type=int, default=0,
                     help="rows per GEMM row tile (moe_config.chunk_rows); 0: tuned per workload")
+    ap.add_argument("--ring-rows", type=int, default=0,
+                    help="ring capacity in rows with --flags 2 (ring dispatch); 0: the workload's own, else 16384")
+    ap.add_argument("--producers", type=int, default=0, help="ring producer workgroups (0: 32)")
     ap.add_argument("--no-tune", action="store_true",
                     help="skip the per-workload tuning (chunk_rows 256, backward branch on a second stream)")
     args = ap.parse_args()
@@ -292,7 +295,10 @@ def main() -> int:
     flags = args.flags | (moe.MOE_F_FORWARD_ONLY if fwd_only else 0) | (moe.MOE_F_UNFUSED if args.unfused else 0)
     t0 = time.time()
     inp = moe_inputs.layer_inputs(cfg, with_dy=not fwd_only)
-    layer = MoeLayer.from_config(cfg, with_backward=not fwd_only, flags=flags)
+    ring_kw = {}
+    if flags & moe.MOE_F_RING_DISPATCH:
+        ring_kw = dict(ring_rows=args.ring_rows or cfg.ring_rows, producer_wgs=args.producers)
+    layer = MoeLayer.from_config(cfg, with_backward=not fwd_only, flags=flags, **ring_kw)
     layer.set_inputs(inp.x_bits, inp.w_r_bits, inp.bias, None if fwd_only else inp.dy_bits)
     log(f"[bench] inputs on device; drawing and quantising {cfg.E + cfg.n_shared} experts")
     layer.load_experts(moe_inputs.iter_expert_weights(cfg, threads=min(16, os.cpu_count() or 8)))
@@ -447,7 +453,9 @@ def main() -> int:
                                 f"I={cfg.inter} {cfg.score}, seed {cfg.seed}"),
                    "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "inter": cfg.inter, "score": cfg.score,
                    "n_shared": cfg.n_shared, "seed": cfg.seed, "parallelism": "single GPU",
-                   "path": "unfused" if args.unfused else "fused", **knobs},
+                   "path": "unfused" if args.unfused else ("ring" if ring_kw else "fused"), **knobs,
+                   **({"ring_rows": int(layer.cfg.ring_rows) or 16384, "producer_wgs": int(layer.cfg.producer_wgs) or 32}
+                      if ring_kw else {})},
         "tuning": tuning,
         "tflops": round(tflops, 2),
         "mfma_frac_layer": round(flops_gemm / (ms * 1e-3) / MXFP8_PEAK, 4),

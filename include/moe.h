@@ -78,18 +78,26 @@ typedef struct moe_config {
   int32_t inter;      /* SwiGLU intermediate size I */
   int32_t n_shared;   /* always-on shared experts (weight 1), stored after the E routed ones */
   int32_t score_fn;   /* moe_score_fn */
-  int32_t ring_rows;  /* ring token buffer capacity in rows (0 = default; multiple of 256) */
-  int32_t chunk_rows; /* rows per GEMM row tile at most (0 = 256; a multiple of 32 up to 256;
-                         the ring dispatch takes 256 only) */
-  int32_t producer_wgs; /* gather (producer) workgroups of the persistent dispatch kernel (0 = default, max 128) */
+  int32_t ring_rows;  /* ring token buffer capacity in rows (0 = 16384; a multiple of the row-tile
+                         height chunk_rows, at least one tile) */
+  int32_t chunk_rows; /* rows per GEMM row tile at most (0 = 256; a multiple of 32 up to 256);
+                         with the ring dispatch also the rows of one ring slot */
+  int32_t producer_wgs; /* workgroups gathering rows into the ring (0 = 32, max 128) */
   uint32_t flags;     /* MOE_F_* */
 } moe_config;
 
 /* Forward dispatch.  By default the gate/up GEMM pulls its rows straight from the quantised
  * activations through the schedule (MOE_F_DIRECT_GATHER names that default explicitly).
- * MOE_F_RING_DISPATCH asks for the persistent producer/consumer kernel fed through the ring
- * token buffer instead; it is currently rejected with MOE_EINVAL (disabled while a device
- * memory fault seen with its consumer is investigated).  Both flags together: MOE_EINVAL. */
+ * MOE_F_RING_DISPATCH stages them instead in the fixed-capacity ring token buffer of the
+ * workspace, reused cyclically (knowledge card "Mixture-of-Kittens——面向NVL72的开源MoE训练
+ * megakernel", 方法/产品要点: ring buffers, pull dispatch; article "Cursor 為 Composer 改造 MoE
+ * 訓練…", section "MoK 將運算同通訊塞入同一個核心": part of the GPU moves data while the rest
+ * computes): the chunks (GEMM row tiles, one per slot of chunk_rows rows) go in rounds of half
+ * the slots; producer_wgs workgroups on the library's second stream gather a round's rows into
+ * its slots while the gate/up GEMM on the caller's stream runs the previous round from the
+ * other half, ordered by events (no device-side waits, no host synchronisation).  Every row is
+ * processed at any capacity down to one slot, and the results are bitwise those of direct
+ * gather.  Both flags together: MOE_EINVAL. */
 #define MOE_F_DIRECT_GATHER 1u
 #define MOE_F_RING_DISPATCH 2u
 
@@ -163,9 +171,9 @@ typedef struct moe_saved_layout {
  * so that tests can read the stage results of the backward pass).  ld = tok_stride. */
 typedef struct moe_workspace_layout {
   size_t status;     /* int32              device status word (MOE_DEV_*), sticky */
-  size_t ring;       /* fp8   [slots, 256, d] ring token buffer (ring dispatch only) */
-  size_t ring_s;     /* e8m0  [slots, 256, d/32] */
-  size_t ring_flags; /* int32 [2 slots + 1] */
+  size_t ring;       /* fp8   [slots, chunk_rows, d] ring token buffer (ring dispatch only) */
+  size_t ring_s;     /* e8m0  [slots, chunk_rows, d/32] */
+  size_t ring_flags; /* int32 [2 slots + 1] (unused by the stream-ordered ring; kept for layout) */
   size_t blkcnt;     /* int32 [ceil(T/64), E] per-block expert counts, then their scans */
   size_t dyq;        /* fp8   [T, d]       dy quantised along d */
   size_t dys;        /* e8m0  [T, d/32] */

@@ -8,7 +8,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_mi355x.so")
-SOURCES = ["api.hip", "gemm.hip", "quant.hip", "router.hip", "combine.hip", "ring.hip", "unfused.hip", "probe.hip"]
+SOURCES = ["api.hip", "gemm.hip", "quant.hip", "router.hip", "combine.hip", "ring.hip", "ring_dispatch.hip", "unfused.hip", "probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",

@@ -1,6 +1,8 @@
 // Host side of the C ABI: validation, buffer layout, kernel sequence.  Nothing here blocks the
 // host or allocates device memory; every launch goes to the caller's stream.
+#include <algorithm>
 #include <mutex>
+#include <vector>
 
 #include "../../include/moe.h"
 #include "kernels.h"
@@ -23,7 +25,6 @@ struct Dims {
 constexpr int kChunkRows = 256;      // rows per ring slot: one GEMM row tile at most
 constexpr int kDefaultRingRows = 16384;
 constexpr int kDefaultProducers = 32;
-constexpr int kSpinLimit = 1 << 22;  // bounded waits of the ring kernel (~seconds)
 
 Dims dims(const moe_config& c) {
   Dims m;
@@ -38,7 +39,7 @@ Dims dims(const moe_config& c) {
   m.tile64_bound = m.ld_tok / 64;
   // the ring buffer exists only for the ring dispatch
   const int64_t ring_rows = !(c.flags & MOE_F_RING_DISPATCH) ? 0 : c.ring_rows ? c.ring_rows : kDefaultRingRows;
-  m.nslots = ring_rows / kChunkRows;
+  m.nslots = ring_rows / m.tile_rows;  // a slot holds one chunk: one row tile
   m.producers = c.producer_wgs ? c.producer_wgs : kDefaultProducers;
   m.unfused = (c.flags & MOE_F_UNFUSED) != 0;
   return m;
@@ -56,14 +57,13 @@ moe_status check_config(const moe_config* c) {
   if (c->score_fn != MOE_SCORE_SOFTMAX && c->score_fn != MOE_SCORE_SIGMOID) return MOE_EINVAL;
   if (c->flags & ~kKnownFlags) return MOE_EINVAL;
   if ((c->flags & MOE_F_DIRECT_GATHER) && (c->flags & MOE_F_RING_DISPATCH)) return MOE_EINVAL;
-  if (c->flags & MOE_F_RING_DISPATCH) return MOE_EINVAL;  // disabled: see the ring kernel's header
-  // the tuning knobs only act on the ring dispatch
+  // ring capacity and producer workgroups act on the ring dispatch only
   if (!(c->flags & MOE_F_RING_DISPATCH) && (c->ring_rows || c->producer_wgs)) return MOE_EINVAL;
   if (c->ring_rows < 0 || c->producer_wgs < 0 || c->producer_wgs > 128) return MOE_ESHAPE;
-  if (c->ring_rows && (c->ring_rows < kChunkRows || c->ring_rows % kChunkRows)) return MOE_ESHAPE;
-  // rows per GEMM row tile: every path; the ring's slots hold whole 256-row tiles
+  // rows per GEMM row tile (every path; a ring slot holds one tile)
   if (c->chunk_rows < 0 || c->chunk_rows > kChunkRows || c->chunk_rows % 32) return MOE_ESHAPE;
-  if ((c->flags & MOE_F_RING_DISPATCH) && c->chunk_rows && c->chunk_rows != kChunkRows) return MOE_ESHAPE;
+  const int64_t slot_rows = c->chunk_rows ? c->chunk_rows : kChunkRows;
+  if (c->ring_rows && (c->ring_rows < slot_rows || c->ring_rows % slot_rows)) return MOE_ESHAPE;
   const int64_t RS = (int64_t)c->T * c->k + (int64_t)c->n_shared * c->T;
   if (RS >= (1ll << 30)) return MOE_ESHAPE;
   // operands addressed with 32-bit byte offsets from one base: the gathered activations
@@ -125,8 +125,8 @@ moe_workspace_layout work_layout(const Dims& m) {
   moe_workspace_layout w{};
   Layout L;
   w.status = L.take(64);
-  w.ring = L.take(m.nslots * kChunkRows * m.d);
-  w.ring_s = L.take(m.nslots * kChunkRows * m.d / 32);
+  w.ring = L.take(m.nslots * m.tile_rows * m.d);
+  w.ring_s = L.take(m.nslots * m.tile_rows * m.d / 32);
   w.ring_flags = L.take(4 * (2 * m.nslots + 1));
   w.blkcnt = L.take(4 * m.nblk * m.E);
   w.dyq = L.take(m.T * m.d);
@@ -188,6 +188,26 @@ struct SideStream {
 };
 constexpr int kMaxDevices = 64;
 thread_local SideStream t_side[kMaxDevices];
+
+// Events that order the ring dispatch's rounds, per host thread and device (created on first
+// use, kept until the process ends).
+struct RingEvents {
+  std::vector<hipEvent_t> prod, cons;
+  bool ensure(size_t n) {
+    while (prod.size() < n) {
+      hipEvent_t a = nullptr, b = nullptr;
+      if (hipEventCreateWithFlags(&a, hipEventDisableTiming) != hipSuccess) return false;
+      if (hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess) {
+        hipEventDestroy(a);
+        return false;
+      }
+      prod.push_back(a);
+      cons.push_back(b);
+    }
+    return true;
+  }
+};
+thread_local RingEvents t_ring_events[kMaxDevices];
 
 SideStream* side_stream() {
   int dev = 0;
@@ -363,31 +383,42 @@ moe_status forward_impl(const moe_config* cfg, const Dims& m, const moe_saved_la
   if (!(cfg->flags & MOE_F_RING_DISPATCH)) {
     MOE_TRY(launch_gemm_gateup(ga, (int)m.tiles_bound, stream));
   } else {
-    if (ring_max_resident() <= m.producers) return MOE_ESHAPE;
-    RingArgs ra;
-    ra.s = sv;
-    ra.xq = xq;
-    ra.xs = xs;
-    ra.w1q = w1q;
-    ra.w1s = w1s;
-    ra.g = ga.g;
-    ra.u = ga.u;
-    ra.hq = ga.hq;
-    ra.hs = ga.hs;
-    ra.ring = sc.ring;
-    ra.ring_s = sc.ring_s;
-    ra.flags = sc.ring_flags;
-    ra.n_flags = (int)(2 * m.nslots + 1);
-    ra.ready = ra.flags;
-    ra.done = ra.flags + m.nslots;
-    ra.abort_flag = ra.flags + 2 * m.nslots;
-    ra.status = status;
-    ra.d = d;
-    ra.I = I;
-    ra.nslots = (int)m.nslots;
-    ra.producers = (int)m.producers;
-    ra.spin_limit = kSpinLimit;
-    MOE_TRY(launch_ring_gateup(ra, stream));
+    // Ring dispatch: chunks (row tiles) in rounds of H, chunk c in slot c % nslots.  Round r's
+    // gather (producers, on the second stream) waits for the GEMM of round r - lag, the last
+    // round whose chunks used its slots (lag H <= nslots, so the rounds in between use others);
+    // round r's GEMM (caller's stream) waits for its gather.  The host bounds the chunk count by
+    // tiles_bound; rounds past the schedule's real count find no chunks and return.
+    const int nslots = (int)m.nslots, H = std::max(1, nslots / 2);
+    const int lag = nslots / H;  // ceil((nslots - H + 1) / H)
+    const int rounds = (int)((m.tiles_bound + H - 1) / H);
+    SideStream* side = side_stream();
+    int dev = 0;
+    MOE_TRY(hipGetDevice(&dev));
+    RingEvents& ev = t_ring_events[dev % kMaxDevices];
+    const size_t K = (size_t)lag + 2;  // event r % K is recorded again only after round r - lag's wait
+    if (side && !ev.ensure(K)) return MOE_ELAUNCH;
+    hipStream_t ps = side ? side->st : stream;
+    if (side) {
+      MOE_TRY(hipEventRecord(side->fork, stream));  // xq, xs and the schedule are ready
+      MOE_TRY(hipStreamWaitEvent(ps, side->fork, 0));
+    }
+    ga.ring = sc.ring;
+    ga.ring_s = sc.ring_s;
+    ga.nslots = nslots;
+    ga.slot_rows = (int)m.tile_rows;
+    ga.nchunks = H;
+    for (int r = 0; r < rounds; ++r) {
+      if (side && r >= lag) MOE_TRY(hipStreamWaitEvent(ps, ev.cons[(r - lag) % K], 0));
+      MOE_TRY(launch_ring_gather(sv, xq, xs, d, sc.ring, sc.ring_s, (int)m.tile_rows, nslots, r * H, H,
+                                 (int)m.producers, ps));
+      if (side) {
+        MOE_TRY(hipEventRecord(ev.prod[r % K], ps));
+        MOE_TRY(hipStreamWaitEvent(stream, ev.prod[r % K], 0));
+      }
+      ga.chunk0 = r * H;
+      MOE_TRY(launch_gemm_gateup(ga, H, stream));
+      if (side) MOE_TRY(hipEventRecord(ev.cons[r % K], stream));
+    }
   }
   mark(stream, MOE_PH_GATEUP);
 

@@ -52,10 +52,23 @@ __global__ __launch_bounds__(512, 1) void k_gemm_gateup(GateUpArgs p) {
   extern __shared__ __align__(16) uint8_t lds[];
   const SchedView& s = p.s;
   const int I = p.I, d = p.d, NT = I / 128;
-  int item;
-  if (!xcd_item(s.tile_start[s.n_exp] * NT, &item)) return;
-  int nt;
-  const RowTile rt = item_tile(s, item, NT, &nt);
+  int item, nt;
+  RowTile rt;
+  const uint8_t *ra = nullptr, *ras = nullptr;  // ring dispatch: the chunk's slot
+  if (p.ring) {
+    // the round's chunks (those that exist), column tiles fastest
+    const int nc = min(p.nchunks, s.tile_start[s.n_exp] - p.chunk0);
+    if (nc <= 0 || !xcd_item(nc * NT, &item)) return;
+    const int c = p.chunk0 + item / NT;
+    nt = item - (item / NT) * NT;
+    rt = row_tile(s, c);
+    const size_t slot = (size_t)(c % p.nslots) * p.slot_rows;
+    ra = p.ring + slot * d;
+    ras = p.ring_s + slot * (d / 32);
+  } else {
+    if (!xcd_item(s.tile_start[s.n_exp] * NT, &item)) return;
+    rt = item_tile(s, item, NT, &nt);
+  }
   if (rt.rows <= 0) return;
   const int n0 = nt * 128;
   const uint8_t* w1 = p.w1q + (size_t)rt.e * 2 * I * d;
@@ -80,10 +93,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm_gateup(GateUpArgs p) {
   };
   dispatch_rows(rt.rows, [&]<int F>() {
     TileLoads8<F> L;
-    L.init(p.xq, [&](int r) { return p.xq + (size_t)arow(r) * d; },
-           w1, [&](int r) { return w1 + (size_t)gateup_brow(r, n0, I) * d; },
-           p.xs, [&](int r) { return p.xs + (size_t)arow(r) * (d / 32); },
-           w1s, [&](int r) { return w1s + (size_t)gateup_brow(r, n0, I) * (d / 32); });
+    if (ra) {  // ring dispatch: the rows sit in the chunk's slot in order
+      L.init(ra, [&](int r) { return ra + (size_t)min(r, last) * d; },
+             w1, [&](int r) { return w1 + (size_t)gateup_brow(r, n0, I) * d; },
+             ras, [&](int r) { return ras + (size_t)min(r, last) * (d / 32); },
+             w1s, [&](int r) { return w1s + (size_t)gateup_brow(r, n0, I) * (d / 32); });
+    } else {
+      L.init(p.xq, [&](int r) { return p.xq + (size_t)arow(r) * d; },
+             w1, [&](int r) { return w1 + (size_t)gateup_brow(r, n0, I) * d; },
+             p.xs, [&](int r) { return p.xs + (size_t)arow(r) * (d / 32); },
+             w1s, [&](int r) { return w1s + (size_t)gateup_brow(r, n0, I) * (d / 32); });
+    }
     v16f acc[(F + 1) / 2][2];
     mainloop8<F>(lds, L, d / KS, acc, side);
     if (p.hq)

@@ -27,6 +27,11 @@ struct GateUpArgs {
   uint8_t *w1t, *w1ts;  // [NX][d][2I] + [NX][2I/128][d][4]: W1 transposed, requantised along 2I (NULL: skip)
   int d, I;
   int contiguous;
+  // ring dispatch (ring != NULL): the launch runs chunks [chunk0, chunk0 + nchunks) (chunk =
+  // row tile), whose rows the producers staged in slot c % nslots: ring [nslots][slot_rows][d],
+  // ring_s [nslots][slot_rows][d/32]
+  const uint8_t *ring, *ring_s;
+  int chunk0, nchunks, nslots, slot_rows;
 };
 
 struct DownArgs {
@@ -84,6 +89,10 @@ hipError_t ring_init();
 int ring_max_resident();
 hipError_t launch_ring_gateup(const RingArgs&, hipStream_t);
 hipError_t launch_gemm_gateup(const GateUpArgs&, int tiles_bound, hipStream_t);
+// Producer side of the ring dispatch: rows of chunks [chunk0, chunk0 + nchunks) into their slots.
+hipError_t launch_ring_gather(const SchedView& s, const uint8_t* xq, const uint8_t* xs, int d, uint8_t* ring,
+                              uint8_t* ring_s, int slot_rows, int nslots, int chunk0, int nchunks, int producers,
+                              hipStream_t st);
 hipError_t launch_gemm_down(const DownArgs&, int tiles_bound, hipStream_t);
 hipError_t launch_gemm_dgrad_down(const DgradDownArgs&, int tiles_bound, hipStream_t);
 hipError_t launch_gemm_dgrad_gateup(const DgradGateUpArgs&, int tiles_bound, hipStream_t);

@@ -20,9 +20,10 @@
 // cannot deadlock.  Every wait is bounded: past `spin_limit` polls the kernel records a status
 // code and all workgroups leave their loops.  Results are bitwise those of the direct kernel.
 //
-// Status: not launched.  The library rejects MOE_F_RING_DISPATCH: the first device run of this
-// consumer (tile code out of line in consume_tile) ended in a memory fault whose cause has not
-// been identified; a host build of the kernel finds every access in bounds.
+// Status: not launched.  The first device run of this consumer (tile code out of line in
+// consume_tile) ended in a memory fault whose cause has not been identified; a host build of the
+// kernel finds every access in bounds.  MOE_F_RING_DISPATCH runs the stream-ordered ring of
+// ring_dispatch.hip instead (producer and consumer kernels ordered by events, no device waits).
 #include "common.h"
 #include "gemm_core.h"
 #include "kernels.h"

@@ -39,6 +39,18 @@ def test_header_structs_match_the_binding():
     assert fields == [f for f, _ in moe.moe_config._fields_]
 
 
+@pytest.mark.parametrize("kw", [dict(), dict(ring_rows=256), dict(ring_rows=2048, producer_wgs=8),
+                                dict(ring_rows=384, chunk_rows=128, producer_wgs=128)])
+def test_ring_dispatch_configurations_are_accepted(kw):
+    """The ring dispatch takes any whole number of slots (one chunk of chunk_rows rows each) and
+    up to 128 producer workgroups; its buffer lives in the workspace."""
+    ws0, _, wl0 = moe.moe_query(moe.make_config(4096, 256, 8, 2, 128), with_workspace_layout=True)
+    ws, _, wl = moe.moe_query(moe.make_config(4096, 256, 8, 2, 128, flags=moe.MOE_F_RING_DISPATCH, **kw),
+                              with_workspace_layout=True)
+    slots = (kw.get("ring_rows") or 16384) // (kw.get("chunk_rows") or 256)
+    assert wl.ring_s - wl.ring >= slots * (kw.get("chunk_rows") or 256) * 256 and ws > ws0
+
+
 @pytest.mark.parametrize("rows", [32, 64, 96, 128, 192, 256])
 def test_row_tile_heights_are_accepted_on_the_direct_path(rows):
     """chunk_rows (rows per GEMM row tile) is a tuning knob of every path and leaves the buffer
@@ -84,7 +96,10 @@ def test_forward_only_layout_drops_transposed_weights():
     (dict(chunk_rows=16), moe.MOE_ESHAPE),
     (dict(chunk_rows=288), moe.MOE_ESHAPE),  # ... up to 256
     (dict(chunk_rows=-32), moe.MOE_ESHAPE),
-    (dict(flags=2), moe.MOE_EINVAL),         # ring dispatch is disabled
+    (dict(flags=2, ring_rows=300), moe.MOE_ESHAPE),   # ring: whole slots of chunk_rows rows
+    (dict(flags=2, ring_rows=128), moe.MOE_ESHAPE),   # ... at least one
+    (dict(flags=2, chunk_rows=128, ring_rows=192), moe.MOE_ESHAPE),
+    (dict(flags=2, producer_wgs=129), moe.MOE_ESHAPE),
     (dict(flags=3), moe.MOE_EINVAL),         # direct gather and ring dispatch together
     (dict(flags=64), moe.MOE_EINVAL),        # unknown flag
     (dict(flags=32), moe.MOE_EINVAL),        # the unfused forward needs MOE_F_FORWARD_ONLY
