@@ -270,7 +270,7 @@ def main() -> int:
                     help="rows per GEMM row tile (moe_config.chunk_rows); 0: tuned per workload")
     ap.add_argument("--ring-rows", type=int, default=0,
                     help="ring capacity in rows with --flags 2 (ring dispatch); 0: the workload's own, else 16384")
-    ap.add_argument("--producers", type=int, default=0, help="ring producer workgroups (0: 32)")
+    ap.add_argument("--producers", type=int, default=0, help="ring producer workgroups (0: 128)")
     ap.add_argument("--no-tune", action="store_true",
                     help="skip the per-workload tuning (chunk_rows 256, backward branch on a second stream)")
     args = ap.parse_args()
@@ -312,7 +312,13 @@ def main() -> int:
     elif not args.no_tune:
         from mixture_experts_layer_schedule_amd import tune as tuner
         t_tune = time.time()
-        res = tuner.tune(layer, backward=not fwd_only, steps=3, warmup=1, stream=stream)
+        cands = None
+        if ring_kw and args.producers:   # a producer count given on the command line stays
+            ring = int(layer.cfg.ring_rows) or 16384
+            cands = list(dict.fromkeys(
+                tuner.Knobs(kn.chunk_rows, kn.serial_bwd, args.producers)
+                for kn in tuner.candidates(layer.T, layer.E, layer.k, layer.S, not fwd_only, ring)))
+        res = tuner.tune(layer, backward=not fwd_only, steps=3, warmup=1, stream=stream, cands=cands)
         tuning = {"chosen": res.best.label(), "ms_per_step": res.table(),
                   "how": "each candidate timed for 3 steps after 1 warm-up step on the same inputs; "
                          "the default (first) stays unless beaten by more than 1 %"}
@@ -320,6 +326,8 @@ def main() -> int:
             f"({', '.join(f'{k} {v:.2f}' for k, v in list(res.table().items())[:4])} ms)")
     knobs = {"chunk_rows": int(layer.cfg.chunk_rows) or 256,
              "serial_bwd": bool(layer.cfg.flags & moe.MOE_F_SERIAL_BWD)}
+    if ring_kw:
+        knobs["producer_wgs"] = int(layer.cfg.producer_wgs) or 128
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -454,8 +462,7 @@ def main() -> int:
                    "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "inter": cfg.inter, "score": cfg.score,
                    "n_shared": cfg.n_shared, "seed": cfg.seed, "parallelism": "single GPU",
                    "path": "unfused" if args.unfused else ("ring" if ring_kw else "fused"), **knobs,
-                   **({"ring_rows": int(layer.cfg.ring_rows) or 16384, "producer_wgs": int(layer.cfg.producer_wgs) or 32}
-                      if ring_kw else {})},
+                   **({"ring_rows": int(layer.cfg.ring_rows) or 16384} if ring_kw else {})},
         "tuning": tuning,
         "tflops": round(tflops, 2),
         "mfma_frac_layer": round(flops_gemm / (ms * 1e-3) / MXFP8_PEAK, 4),

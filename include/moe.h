@@ -82,7 +82,7 @@ typedef struct moe_config {
                          height chunk_rows, at least one tile) */
   int32_t chunk_rows; /* rows per GEMM row tile at most (0 = 256; a multiple of 32 up to 256);
                          with the ring dispatch also the rows of one ring slot */
-  int32_t producer_wgs; /* workgroups gathering rows into the ring (0 = 32, max 128) */
+  int32_t producer_wgs; /* workgroups gathering rows into the ring (0 = 128, max 128) */
   uint32_t flags;     /* MOE_F_* */
 } moe_config;
 
@@ -171,9 +171,11 @@ typedef struct moe_saved_layout {
  * so that tests can read the stage results of the backward pass).  ld = tok_stride. */
 typedef struct moe_workspace_layout {
   size_t status;     /* int32              device status word (MOE_DEV_*), sticky */
-  size_t ring;       /* fp8   [slots, chunk_rows, d] ring token buffer (ring dispatch only) */
-  size_t ring_s;     /* e8m0  [slots, chunk_rows, d/32] */
-  size_t ring_flags; /* int32 [2 slots + 1] (unused by the stream-ordered ring; kept for layout) */
+  size_t ring;       /* fp8   [ring_rows, d] ring token buffer (ring dispatch only): ring_rows /
+                        chunk_rows slots of chunk_rows rows; sized by ring_rows alone, so one
+                        workspace serves every chunk_rows */
+  size_t ring_s;     /* e8m0  [ring_rows, d/32] */
+  size_t ring_flags; /* int32 [2 ring_rows/32 + 1] (unused by the stream-ordered ring; kept for layout) */
   size_t blkcnt;     /* int32 [ceil(T/64), E] per-block expert counts, then their scans */
   size_t dyq;        /* fp8   [T, d]       dy quantised along d */
   size_t dys;        /* e8m0  [T, d/32] */

@@ -17,14 +17,14 @@ size_t up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Dims {
   int64_t T, d, E, k, I, S, NX, R, RS, nblk, ld_tok, tiles_bound, tile64_bound;
-  int64_t nslots, producers;
+  int64_t ring_rows, nslots, producers;
   int64_t tile_rows;  // rows per GEMM row tile at most (chunk_rows)
   bool unfused;
 };
 
 constexpr int kChunkRows = 256;      // rows per ring slot: one GEMM row tile at most
 constexpr int kDefaultRingRows = 16384;
-constexpr int kDefaultProducers = 32;
+constexpr int kDefaultProducers = 128;
 
 Dims dims(const moe_config& c) {
   Dims m;
@@ -39,6 +39,7 @@ Dims dims(const moe_config& c) {
   m.tile64_bound = m.ld_tok / 64;
   // the ring buffer exists only for the ring dispatch
   const int64_t ring_rows = !(c.flags & MOE_F_RING_DISPATCH) ? 0 : c.ring_rows ? c.ring_rows : kDefaultRingRows;
+  m.ring_rows = ring_rows;
   m.nslots = ring_rows / m.tile_rows;  // a slot holds one chunk: one row tile
   m.producers = c.producer_wgs ? c.producer_wgs : kDefaultProducers;
   m.unfused = (c.flags & MOE_F_UNFUSED) != 0;
@@ -125,9 +126,11 @@ moe_workspace_layout work_layout(const Dims& m) {
   moe_workspace_layout w{};
   Layout L;
   w.status = L.take(64);
-  w.ring = L.take(m.nslots * m.tile_rows * m.d);
-  w.ring_s = L.take(m.nslots * m.tile_rows * m.d / 32);
-  w.ring_flags = L.take(4 * (2 * m.nslots + 1));
+  // sized by the capacity alone (the most slots any row-tile height gives for the flags), so
+  // that one workspace serves every chunk_rows
+  w.ring = L.take(m.ring_rows * m.d);
+  w.ring_s = L.take(m.ring_rows * m.d / 32);
+  w.ring_flags = L.take(4 * (2 * (m.ring_rows / 32) + 1));
   w.blkcnt = L.take(4 * m.nblk * m.E);
   w.dyq = L.take(m.T * m.d);
   w.dys = L.take(m.T * m.d / 32);

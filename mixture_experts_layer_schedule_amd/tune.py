@@ -9,7 +9,11 @@ section "2.37 倍同 1.41 倍係兩份成績").  On one MI355X with direct gathe
   extra tile;
 * the backward schedule -- the token-axis requantisation of X, H, w*dY and the dW2 GEMM on a
   second stream beside the dgrad chain (the default), or every kernel in launch order
-  (``MOE_F_SERIAL_BWD``).
+  (``MOE_F_SERIAL_BWD``);
+* with the ring dispatch (``MOE_F_RING_DISPATCH``), ``producer_wgs`` -- the workgroups that
+  gather rows into the ring while the GEMM computes (the pages' SMs given to data movement).  The
+  ring capacity is the caller's memory budget and stays as configured; only row-tile heights
+  that divide it are tried.
 
 Every candidate produces the same bits (the library guarantees it), so the tuner only times
 them on the caller's own layer and inputs and keeps the fastest; the first candidate (the
@@ -21,18 +25,21 @@ from __future__ import annotations
 
 from dataclasses import dataclass, field
 
-from . import MOE_F_SERIAL_BWD
+from . import MOE_F_RING_DISPATCH, MOE_F_SERIAL_BWD
 
 CHUNK_ROWS = (256, 192, 128, 96, 64, 32)
+PRODUCERS = (128, 64, 32, 16, 8)   # the library default first
 
 
 @dataclass(frozen=True)
 class Knobs:
     chunk_rows: int = 256
     serial_bwd: bool = False
+    producer_wgs: int = 0   # ring dispatch only (0: not a ring candidate)
 
     def label(self) -> str:
-        return f"chunk_rows={self.chunk_rows}" + (" serial_bwd" if self.serial_bwd else "")
+        return (f"chunk_rows={self.chunk_rows}" + (" serial_bwd" if self.serial_bwd else "")
+                + (f" producers={self.producer_wgs}" if self.producer_wgs else ""))
 
 
 @dataclass
@@ -44,21 +51,31 @@ class TuneResult:
         return {k.label(): round(v, 4) for k, v in sorted(self.ms.items(), key=lambda kv: kv[1])}
 
 
-def candidates(T: int, E: int, k: int, n_shared: int, backward: bool) -> list[Knobs]:
+def candidates(T: int, E: int, k: int, n_shared: int, backward: bool, ring_rows: int = 0) -> list[Knobs]:
     """Knob settings worth timing for a shape.  A tile taller than the largest possible expert
     (T rows for a routed expert, T for the shared one) behaves like that expert's own height,
-    so heights above the smallest multiple of 32 holding T rows are dropped."""
+    so heights above the smallest multiple of 32 holding T rows are dropped.  With a ring of
+    ring_rows rows: heights that divide it, every producer count at the first height, the
+    default producer count at the others."""
     cap = max(32, min(256, -(-T // 32) * 32))
     chunks = [c for c in CHUNK_ROWS if c <= cap] or [cap]
     if cap not in chunks:
         chunks.insert(0, cap)
     serial = (False, True) if backward else (False,)
-    return [Knobs(c, s) for c in chunks for s in serial]
+    if not ring_rows:
+        return [Knobs(c, s) for c in chunks for s in serial]
+    chunks = [c for c in chunks if ring_rows % c == 0] or [32]
+    out = [Knobs(chunks[0], s, p) for p in PRODUCERS for s in serial]
+    out += [Knobs(c, s, PRODUCERS[0]) for c in chunks[1:] for s in serial]
+    return out
 
 
 def apply(cfg, knobs: Knobs) -> None:
-    """Write the knobs into a moe_config (chunk_rows and the MOE_F_SERIAL_BWD bit)."""
+    """Write the knobs into a moe_config (chunk_rows, producer_wgs when set, and the
+    MOE_F_SERIAL_BWD bit)."""
     cfg.chunk_rows = knobs.chunk_rows
+    if knobs.producer_wgs:
+        cfg.producer_wgs = knobs.producer_wgs
     if knobs.serial_bwd:
         cfg.flags |= MOE_F_SERIAL_BWD
     else:
@@ -72,7 +89,8 @@ def tune(layer, backward: bool = True, steps: int = 3, warmup: int = 1, stream=N
     (a fraction of its time), else the first.  timer(step_fn, steps) -> ms per step; by default
     device events around `steps` calls on `stream` after `warmup` untimed ones."""
     if cands is None:
-        cands = candidates(layer.T, layer.E, layer.k, layer.S, backward)
+        ring = (layer.cfg.ring_rows or 16384) if layer.cfg.flags & MOE_F_RING_DISPATCH else 0
+        cands = candidates(layer.T, layer.E, layer.k, layer.S, backward, ring)
 
     def step():
         layer.forward(stream)

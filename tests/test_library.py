@@ -51,6 +51,16 @@ def test_ring_dispatch_configurations_are_accepted(kw):
     assert wl.ring_s - wl.ring >= slots * (kw.get("chunk_rows") or 256) * 256 and ws > ws0
 
 
+def test_ring_workspace_does_not_depend_on_the_row_tile_height():
+    """The tuner changes chunk_rows on a layer whose workspace is already allocated: the ring's
+    regions are sized by its capacity alone, for every height that divides it."""
+    f = moe.MOE_F_RING_DISPATCH
+    for ring_rows in (2048, 16384):
+        sizes = {moe.moe_query(moe.make_config(4096, 256, 8, 2, 128, ring_rows=ring_rows, chunk_rows=c,
+                                               flags=f))[0] for c in (0, 256, 128, 64, 32)}
+        assert len(sizes) == 1
+
+
 @pytest.mark.parametrize("rows", [32, 64, 96, 128, 192, 256])
 def test_row_tile_heights_are_accepted_on_the_direct_path(rows):
     """chunk_rows (rows per GEMM row tile) is a tuning knob of every path and leaves the buffer
