@@ -93,9 +93,12 @@ typedef struct moe_config {
  * megakernel", 方法/产品要点: ring buffers, pull dispatch; article "Cursor 為 Composer 改造 MoE
  * 訓練…", section "MoK 將運算同通訊塞入同一個核心": part of the GPU moves data while the rest
  * computes): the chunks (GEMM row tiles, one per slot of chunk_rows rows) go in rounds of half
- * the slots; producer_wgs workgroups on the library's second stream gather a round's rows into
+ * the slots; producer_wgs workgroups on a stream of the library's own gather a round's rows into
  * its slots while the gate/up GEMM on the caller's stream runs the previous round from the
- * other half, ordered by events (no device-side waits, no host synchronisation).  Every row is
+ * other half, ordered by events (no device-side waits, no host synchronisation).  moe_bwd does
+ * the same for its pull reverse-combine (same pages: the dY rows each expert needs, staged in
+ * the ring for the dgrad-down GEMM; the producers have a stream of their own beside the
+ * backward's second-stream branch, and MOE_F_SERIAL_BWD puts them in launch order).  Every row is
  * processed at any capacity down to one slot, and the results are bitwise those of direct
  * gather.  Both flags together: MOE_EINVAL. */
 #define MOE_F_DIRECT_GATHER 1u

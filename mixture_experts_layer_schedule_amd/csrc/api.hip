@@ -181,16 +181,19 @@ moe_status ensure_init() {
   return g_init_err == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }
 
-// Second stream of each device for the backward's independent branch, with the fork / join
-// events around it: one set per host thread and device (created on first use, default
-// priority, kept until the process ends), so calls from different threads never share events.
+// Extra streams of each device, with fork / join events around their work: kBranchStream runs
+// the backward's independent branch, kRingStream the ring dispatch's producers (its own, so the
+// backward's producers never queue behind that branch).  One set per host thread and device
+// (created on first use, default priority, kept until the process ends), so calls from
+// different threads never share events.
 struct SideStream {
   hipStream_t st = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
   bool ok = false, tried = false;
 };
 constexpr int kMaxDevices = 64;
-thread_local SideStream t_side[kMaxDevices];
+constexpr int kBranchStream = 0, kRingStream = 1;
+thread_local SideStream t_side[kMaxDevices][2];
 
 // Events that order the ring dispatch's rounds, per host thread and device (created on first
 // use, kept until the process ends).
@@ -212,10 +215,10 @@ struct RingEvents {
 };
 thread_local RingEvents t_ring_events[kMaxDevices];
 
-SideStream* side_stream() {
+SideStream* side_stream(int which) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  SideStream& s = t_side[dev];
+  SideStream& s = t_side[dev][which];
   if (!s.tried) {
     s.tried = true;
     s.ok = hipStreamCreateWithFlags(&s.st, hipStreamNonBlocking) == hipSuccess &&
@@ -278,6 +281,45 @@ struct FwdScratch {
   uint8_t *xp = nullptr, *xps = nullptr;  // unfused forward: rows in expert order
   float* yrows = nullptr;
 };
+
+// Ring dispatch of the rows one grouped GEMM pulls (forward gate/up: xq; backward dgrad-down:
+// dYq).  Chunks (row tiles) go in rounds of H = nslots / 2, chunk c in slot c % nslots.  Round
+// r's gather (producers on the ring stream) waits for the GEMM of round r - lag, the last round
+// whose chunks used its slots (lag = nslots / H, so the rounds in between use others); round r's
+// GEMM, launched by consume(chunk0, nchunks) on the caller's stream, waits for its gather.  The
+// host bounds the chunk count by tiles_bound; rounds past the schedule's real count find no
+// chunks and return.  Without overlap (or without the ring stream) everything runs in launch
+// order on the caller's stream.
+template <class Consume>
+moe_status ring_rounds(const Dims& m, const SchedView& sv, const uint8_t* q, const uint8_t* qs, uint8_t* ring,
+                       uint8_t* ring_s, bool overlap, hipStream_t stream, Consume consume) {
+  const int nslots = (int)m.nslots, H = std::max(1, nslots / 2);
+  const int lag = nslots / H;
+  const int rounds = (int)((m.tiles_bound + H - 1) / H);
+  SideStream* side = overlap ? side_stream(kRingStream) : nullptr;
+  int dev = 0;
+  MOE_TRY(hipGetDevice(&dev));
+  RingEvents& ev = t_ring_events[dev % kMaxDevices];
+  const size_t K = (size_t)lag + 2;  // event r % K is recorded again only after round r - lag's wait
+  if (side && !ev.ensure(K)) return MOE_ELAUNCH;
+  hipStream_t ps = side ? side->st : stream;
+  if (side) {
+    MOE_TRY(hipEventRecord(side->fork, stream));  // the pulled rows and the schedule are ready
+    MOE_TRY(hipStreamWaitEvent(ps, side->fork, 0));
+  }
+  for (int r = 0; r < rounds; ++r) {
+    if (side && r >= lag) MOE_TRY(hipStreamWaitEvent(ps, ev.cons[(r - lag) % K], 0));
+    MOE_TRY(launch_ring_gather(sv, q, qs, (int)m.d, ring, ring_s, (int)m.tile_rows, nslots, r * H, H,
+                               (int)m.producers, ps));
+    if (side) {
+      MOE_TRY(hipEventRecord(ev.prod[r % K], ps));
+      MOE_TRY(hipStreamWaitEvent(stream, ev.prod[r % K], 0));
+    }
+    MOE_TRY(consume(r * H, H));
+    if (side) MOE_TRY(hipEventRecord(ev.cons[r % K], stream));
+  }
+  return MOE_OK;
+}
 
 moe_status forward_impl(const moe_config* cfg, const Dims& m, const moe_saved_layout& sl, const void* x,
                         const void* w_router, const float* router_bias, const uint8_t* w1q, const uint8_t* w1s,
@@ -386,42 +428,17 @@ moe_status forward_impl(const moe_config* cfg, const Dims& m, const moe_saved_la
   if (!(cfg->flags & MOE_F_RING_DISPATCH)) {
     MOE_TRY(launch_gemm_gateup(ga, (int)m.tiles_bound, stream));
   } else {
-    // Ring dispatch: chunks (row tiles) in rounds of H, chunk c in slot c % nslots.  Round r's
-    // gather (producers, on the second stream) waits for the GEMM of round r - lag, the last
-    // round whose chunks used its slots (lag H <= nslots, so the rounds in between use others);
-    // round r's GEMM (caller's stream) waits for its gather.  The host bounds the chunk count by
-    // tiles_bound; rounds past the schedule's real count find no chunks and return.
-    const int nslots = (int)m.nslots, H = std::max(1, nslots / 2);
-    const int lag = nslots / H;  // ceil((nslots - H + 1) / H)
-    const int rounds = (int)((m.tiles_bound + H - 1) / H);
-    SideStream* side = side_stream();
-    int dev = 0;
-    MOE_TRY(hipGetDevice(&dev));
-    RingEvents& ev = t_ring_events[dev % kMaxDevices];
-    const size_t K = (size_t)lag + 2;  // event r % K is recorded again only after round r - lag's wait
-    if (side && !ev.ensure(K)) return MOE_ELAUNCH;
-    hipStream_t ps = side ? side->st : stream;
-    if (side) {
-      MOE_TRY(hipEventRecord(side->fork, stream));  // xq, xs and the schedule are ready
-      MOE_TRY(hipStreamWaitEvent(ps, side->fork, 0));
-    }
     ga.ring = sc.ring;
     ga.ring_s = sc.ring_s;
-    ga.nslots = nslots;
+    ga.nslots = (int)m.nslots;
     ga.slot_rows = (int)m.tile_rows;
-    ga.nchunks = H;
-    for (int r = 0; r < rounds; ++r) {
-      if (side && r >= lag) MOE_TRY(hipStreamWaitEvent(ps, ev.cons[(r - lag) % K], 0));
-      MOE_TRY(launch_ring_gather(sv, xq, xs, d, sc.ring, sc.ring_s, (int)m.tile_rows, nslots, r * H, H,
-                                 (int)m.producers, ps));
-      if (side) {
-        MOE_TRY(hipEventRecord(ev.prod[r % K], ps));
-        MOE_TRY(hipStreamWaitEvent(stream, ev.prod[r % K], 0));
-      }
-      ga.chunk0 = r * H;
-      MOE_TRY(launch_gemm_gateup(ga, H, stream));
-      if (side) MOE_TRY(hipEventRecord(ev.cons[r % K], stream));
-    }
+    moe_status st;
+    if ((st = ring_rounds(m, sv, xq, xs, sc.ring, sc.ring_s, true, stream, [&](int chunk0, int nchunks) {
+           ga.chunk0 = chunk0;
+           ga.nchunks = nchunks;
+           return launch_gemm_gateup(ga, nchunks, stream);
+         })) != MOE_OK)
+      return st;
   }
   mark(stream, MOE_PH_GATEUP);
 
@@ -569,16 +586,16 @@ moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const v
   // only on the forward's saved rows and on dy: they run on the device's second stream, beside
   // the router backward and the dgrad chain (whose buffers they do not touch), and are joined
   // before dW1.  MOE_F_SERIAL_BWD (or no second stream) keeps everything in launch order.
-  SideStream* side = (cfg->flags & MOE_F_SERIAL_BWD) ? nullptr : side_stream();
+  SideStream* side = (cfg->flags & MOE_F_SERIAL_BWD) ? nullptr : side_stream(kBranchStream);
   hipStream_t sst = side ? side->st : stream;
-  TokArgs ta;
+  TokArgs ta{};
   ta.s = sv;
   ta.w = w;
   ta.tok_off = tok_off;
   ta.tile64 = tile64;
   ta.ld = m.ld_tok;
   const int tb = (int)m.tile64_bound;
-  WgradArgs wa;
+  WgradArgs wa{};
   wa.tok_off = tok_off;
   wa.ld = m.ld_tok;
   auto side_branch = [&]() -> moe_status {
@@ -620,7 +637,7 @@ moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const v
   // is empty.
   mark(stream, MOE_PH_REQUANT_W);
 
-  DgradDownArgs dd;
+  DgradDownArgs dd{};
   dd.s = sv;
   dd.dyq = dyq;
   dd.dys = dys;
@@ -633,10 +650,26 @@ moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const v
   dd.dgus = at<uint8_t>(workspace, wl.dgus);
   dd.d = d;
   dd.I = I;
-  MOE_TRY(launch_gemm_dgrad_down(dd, (int)m.tiles_bound, stream));
+  if (!(cfg->flags & MOE_F_RING_DISPATCH)) {
+    MOE_TRY(launch_gemm_dgrad_down(dd, (int)m.tiles_bound, stream));
+  } else {
+    // pull reverse-combine through the ring: the dY rows each expert needs, staged in its slots
+    // (the forward's GEMM rounds that read the ring are all ahead of this call on the stream)
+    dd.ring = at<uint8_t>(workspace, wl.ring);
+    dd.ring_s = at<uint8_t>(workspace, wl.ring_s);
+    dd.nslots = (int)m.nslots;
+    dd.slot_rows = (int)m.tile_rows;
+    if ((st = ring_rounds(m, sv, dyq, dys, at<uint8_t>(workspace, wl.ring), at<uint8_t>(workspace, wl.ring_s),
+                          !(cfg->flags & MOE_F_SERIAL_BWD), stream, [&](int chunk0, int nchunks) {
+                            dd.chunk0 = chunk0;
+                            dd.nchunks = nchunks;
+                            return launch_gemm_dgrad_down(dd, nchunks, stream);
+                          })) != MOE_OK)
+      return st;
+  }
   mark(stream, MOE_PH_DGRAD_DOWN);
 
-  DgradGateUpArgs dg;
+  DgradGateUpArgs dg{};
   dg.s = sv;
   dg.dguq = dd.dguq;
   dg.dgus = dd.dgus;

@@ -183,17 +183,31 @@ __global__ __launch_bounds__(512, 1) void k_gemm_down(DownArgs p) {
 
 // ---------------------------------------------------------------------------------------------
 // Backward dgrad of the down GEMM with the SwiGLU backward in the epilogue:
-// dH = w * (dY_t W2t_e^T) (rows pulled from dYq: reverse-combine), dG = dH U s (1 + G (1 - s)),
+// dH = w * (dY_t W2t_e^T) (rows pulled from dYq: reverse-combine, straight from dYq or, with the
+// ring dispatch, from the ring slots the producers filled), dG = dH U s (1 + G (1 - s)),
 // dU = dH silu(G); [dG dU] quantised along 2I.
 
 __global__ __launch_bounds__(512, 1) void k_gemm_dgrad_down(DgradDownArgs p) {
   extern __shared__ __align__(16) uint8_t lds[];
   const SchedView& s = p.s;
   const int I = p.I, d = p.d, NT = (I + TN - 1) / TN;
-  int item;
-  if (!xcd_item(s.tile_start[s.n_exp] * NT, &item)) return;
-  int nt;
-  const RowTile rt = item_tile(s, item, NT, &nt);
+  int item, nt;
+  RowTile rt;
+  const uint8_t *ra = nullptr, *ras = nullptr;  // ring dispatch: the chunk's slot
+  if (p.ring) {
+    // the round's chunks (those that exist), column tiles fastest
+    const int nc = min(p.nchunks, s.tile_start[s.n_exp] - p.chunk0);
+    if (nc <= 0 || !xcd_item(nc * NT, &item)) return;
+    const int c = p.chunk0 + item / NT;
+    nt = item - (item / NT) * NT;
+    rt = row_tile(s, c);
+    const size_t slot = (size_t)(c % p.nslots) * p.slot_rows;
+    ra = p.ring + slot * d;
+    ras = p.ring_s + slot * (d / 32);
+  } else {
+    if (!xcd_item(s.tile_start[s.n_exp] * NT, &item)) return;
+    rt = item_tile(s, item, NT, &nt);
+  }
   if (rt.rows <= 0) return;
   const int n0 = nt * TN;
   const int last = rt.rows - 1;
@@ -205,10 +219,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dgrad_down(DgradDownArgs p) {
     constexpr int FH = (F + 1) / 2;
     const int m0 = (w >> 2) * FH;
     TileLoads8<F> L;
-    L.init(p.dyq, [&](int r) { return p.dyq + (size_t)row_token(s, rt.r0 + min(r, last)) * d; },
-           w2t, [&](int r) { return w2t + (size_t)min(n0 + r, I - 1) * d; },
-           p.dys, [&](int r) { return p.dys + (size_t)row_token(s, rt.r0 + min(r, last)) * (d / 32); },
-           w2ts, [&](int r) { return w2ts + (size_t)min(n0 + r, I - 1) * 4; });
+    if (ra) {  // ring dispatch: the rows sit in the chunk's slot in order
+      L.init(ra, [&](int r) { return ra + (size_t)min(r, last) * d; },
+             w2t, [&](int r) { return w2t + (size_t)min(n0 + r, I - 1) * d; },
+             ras, [&](int r) { return ras + (size_t)min(r, last) * (d / 32); },
+             w2ts, [&](int r) { return w2ts + (size_t)min(n0 + r, I - 1) * 4; });
+    } else {
+      L.init(p.dyq, [&](int r) { return p.dyq + (size_t)row_token(s, rt.r0 + min(r, last)) * d; },
+             w2t, [&](int r) { return w2t + (size_t)min(n0 + r, I - 1) * d; },
+             p.dys, [&](int r) { return p.dys + (size_t)row_token(s, rt.r0 + min(r, last)) * (d / 32); },
+             w2ts, [&](int r) { return w2ts + (size_t)min(n0 + r, I - 1) * 4; });
+    }
     L.bsk = 4 * I;  // stage-major scales: stage t's words are plane t
     v16f acc[FH][2];
     mainloop8<F, false>(lds, L, d / KS, acc);

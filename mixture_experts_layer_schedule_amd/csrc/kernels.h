@@ -50,6 +50,9 @@ struct DgradDownArgs {
   const float *w, *g, *u;
   uint8_t *dguq, *dgus;
   int d, I;
+  // ring dispatch (ring != NULL): as GateUpArgs, the slots holding dYq / dYs rows
+  const uint8_t *ring, *ring_s;
+  int chunk0, nchunks, nslots, slot_rows;
 };
 
 struct DgradGateUpArgs {

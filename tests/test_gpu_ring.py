@@ -1,6 +1,6 @@
 """Ring token buffers (MOE_F_RING_DISPATCH): producer workgroups on a second stream gather each
-round of chunks (GEMM row tiles) into the fixed-capacity ring while the gate/up GEMM runs the
-previous round from it, ordered by events.  The results are bitwise those of direct gather at
+round of chunks (GEMM row tiles) into the fixed-capacity ring while the gate/up GEMM (forward)
+or the dgrad-down GEMM (backward, dY rows) runs the previous round from it, ordered by events.  The results are bitwise those of direct gather at
 every ring capacity (down to one slot, far below the hottest expert's load, so the ring wraps
 many times) and producer count; no row is dropped.
 """
@@ -79,6 +79,53 @@ def test_ring_with_shorter_chunks(skew, chunk_rows, ring_rows):
     layer = _run(cfg, inp, ws, ring_rows=ring_rows, chunk_rows=chunk_rows, producer_wgs=4, flags=RING)
     for name in ("g", "u", "hq", "hs", "yslot"):
         assert np.array_equal(to_np(layer.saved_tensor(name)), to_np(ref.saved_tensor(name))), name
+
+
+def _run_bwd(cfg, inp, ws, **kw):
+    import torch
+    from mixture_experts_layer_schedule_amd import MoeLayer
+    import mixture_experts_layer_schedule_amd as moe
+
+    layer = MoeLayer.from_config(cfg, with_backward=True, **kw)
+    layer.set_inputs(inp.x_bits, inp.w_r_bits, inp.bias, inp.dy_bits)
+    layer.load_experts((e, w1, w2) for e, (w1, w2) in enumerate(ws))
+    layer.forward()
+    layer.backward()
+    torch.cuda.synchronize()
+    assert moe.moe_device_status(layer.workspace) == 0
+    return layer
+
+
+def _bwd_results(layer):
+    import torch
+    out = {"dx": layer.dx.view(torch.int16), "dx32": layer.dx32, "dw_r": layer.dw_r, "dw1": layer.dw1, "dw2": layer.dw2}
+    for n in ("dguq", "dgus"):
+        out[n] = layer.workspace_tensor(n)
+    return {n: to_np(t) for n, t in out.items()}
+
+
+@pytest.fixture(scope="module", params=[SKEW, WIDE], ids=lambda c: c.name)
+def bwd_ref(request):
+    import mixture_experts_layer_schedule_amd as moe
+    cfg = request.param.with_(backward=True)
+    inp = moe_inputs.layer_inputs(cfg)
+    ws = [moe_inputs.expert_weights(cfg, e) for e in range(cfg.E + cfg.n_shared)]
+    return cfg, inp, ws, _bwd_results(_run_bwd(cfg, inp, ws, flags=moe.MOE_F_DIRECT_GATHER))
+
+
+@pytest.mark.parametrize("ring_rows,producers,serial", [(256, 1, False), (512, 3, True), (768, 16, False),
+                                                        (8192, 32, True)])
+def test_backward_ring_matches_direct_pull(bwd_ref, ring_rows, producers, serial):
+    """The backward's pull reverse-combine through the ring (dY rows staged in the slots for the
+    dgrad-down GEMM), with the producers on their own stream beside the backward's second-stream
+    branch or everything in launch order: [dG dU] codes and scales and every gradient bitwise
+    those of the direct pull."""
+    import mixture_experts_layer_schedule_amd as moe
+    cfg, inp, ws, ref = bwd_ref
+    flags = RING | (moe.MOE_F_SERIAL_BWD if serial else 0)
+    got = _bwd_results(_run_bwd(cfg, inp, ws, ring_rows=ring_rows, producer_wgs=producers, flags=flags))
+    for n, v in ref.items():
+        assert np.array_equal(got[n], v), n
 
 
 def test_kimi_shape_ring_below_peak_load():
