@@ -316,7 +316,7 @@ def main() -> int:
         if ring_kw and args.producers:   # a producer count given on the command line stays
             ring = int(layer.cfg.ring_rows) or 16384
             cands = list(dict.fromkeys(
-                tuner.Knobs(kn.chunk_rows, kn.serial_bwd, args.producers)
+                tuner.Knobs(kn.chunk_rows, kn.serial_bwd, args.producers, kn.ring_rows)
                 for kn in tuner.candidates(layer.T, layer.E, layer.k, layer.S, not fwd_only, ring)))
         res = tuner.tune(layer, backward=not fwd_only, steps=3, warmup=1, stream=stream, cands=cands)
         tuning = {"chosen": res.best.label(), "ms_per_step": res.table(),

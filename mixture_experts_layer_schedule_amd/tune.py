@@ -11,9 +11,11 @@ section "2.37 倍同 1.41 倍係兩份成績").  On one MI355X with direct gathe
   second stream beside the dgrad chain (the default), or every kernel in launch order
   (``MOE_F_SERIAL_BWD``);
 * with the ring dispatch (``MOE_F_RING_DISPATCH``), ``producer_wgs`` -- the workgroups that
-  gather rows into the ring while the GEMM computes (the pages' SMs given to data movement).  The
-  ring capacity is the caller's memory budget and stays as configured; only row-tile heights
-  that divide it are tried.
+  gather rows into the ring while the GEMM computes (the pages' SMs given to data movement) --
+  and ``ring_rows``, the ring's capacity (the pages' buffer capacity).  The configured capacity
+  is the caller's memory budget: the tuner tries it and a half and a quarter of it, never more
+  (a smaller ring fits the workspace sized for the budget), and only row-tile heights that
+  divide the capacity tried.
 
 Every candidate produces the same bits (the library guarantees it), so the tuner only times
 them on the caller's own layer and inputs and keeps the fastest; the first candidate (the
@@ -36,10 +38,12 @@ class Knobs:
     chunk_rows: int = 256
     serial_bwd: bool = False
     producer_wgs: int = 0   # ring dispatch only (0: not a ring candidate)
+    ring_rows: int = 0      # ring dispatch only (0: not a ring candidate)
 
     def label(self) -> str:
         return (f"chunk_rows={self.chunk_rows}" + (" serial_bwd" if self.serial_bwd else "")
-                + (f" producers={self.producer_wgs}" if self.producer_wgs else ""))
+                + (f" producers={self.producer_wgs}" if self.producer_wgs else "")
+                + (f" ring_rows={self.ring_rows}" if self.ring_rows else ""))
 
 
 @dataclass
@@ -56,7 +60,8 @@ def candidates(T: int, E: int, k: int, n_shared: int, backward: bool, ring_rows:
     (T rows for a routed expert, T for the shared one) behaves like that expert's own height,
     so heights above the smallest multiple of 32 holding T rows are dropped.  With a ring of
     ring_rows rows: heights that divide it, every producer count at the first height, the
-    default producer count at the others."""
+    default producer count at the others, then half and a quarter of the capacity (when still a
+    whole number of the first height's slots) at the first height and default producers."""
     cap = max(32, min(256, -(-T // 32) * 32))
     chunks = [c for c in CHUNK_ROWS if c <= cap] or [cap]
     if cap not in chunks:
@@ -65,17 +70,23 @@ def candidates(T: int, E: int, k: int, n_shared: int, backward: bool, ring_rows:
     if not ring_rows:
         return [Knobs(c, s) for c in chunks for s in serial]
     chunks = [c for c in chunks if ring_rows % c == 0] or [32]
-    out = [Knobs(chunks[0], s, p) for p in PRODUCERS for s in serial]
-    out += [Knobs(c, s, PRODUCERS[0]) for c in chunks[1:] for s in serial]
+    out = [Knobs(chunks[0], s, p, ring_rows) for p in PRODUCERS for s in serial]
+    out += [Knobs(c, s, PRODUCERS[0], ring_rows) for c in chunks[1:] for s in serial]
+    for div in (2, 4):
+        cap = ring_rows // div
+        if ring_rows % div == 0 and cap >= chunks[0] and cap % chunks[0] == 0:
+            out += [Knobs(chunks[0], s, PRODUCERS[0], cap) for s in serial]
     return out
 
 
 def apply(cfg, knobs: Knobs) -> None:
-    """Write the knobs into a moe_config (chunk_rows, producer_wgs when set, and the
-    MOE_F_SERIAL_BWD bit)."""
+    """Write the knobs into a moe_config (chunk_rows, producer_wgs and ring_rows when set, and
+    the MOE_F_SERIAL_BWD bit)."""
     cfg.chunk_rows = knobs.chunk_rows
     if knobs.producer_wgs:
         cfg.producer_wgs = knobs.producer_wgs
+    if knobs.ring_rows:
+        cfg.ring_rows = knobs.ring_rows
     if knobs.serial_bwd:
         cfg.flags |= MOE_F_SERIAL_BWD
     else:

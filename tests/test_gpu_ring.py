@@ -128,6 +128,27 @@ def test_backward_ring_matches_direct_pull(bwd_ref, ring_rows, producers, serial
         assert np.array_equal(got[n], v), n
 
 
+def test_ring_tuner_keeps_the_bits(bwd_ref):
+    """The tuner over the ring's knobs (row-tile height, producer workgroups, capacities up to the
+    configured one) runs every candidate in the layer's one workspace and leaves the fastest in
+    its configuration; the tuned layer still computes the direct pull's bits."""
+    import torch
+    from mixture_experts_layer_schedule_amd import tune
+    cfg, inp, ws, ref = bwd_ref
+    layer = _run_bwd(cfg, inp, ws, ring_rows=1024, flags=RING)
+    res = tune.tune(layer, backward=True, steps=1, warmup=1)
+    cands = tune.candidates(layer.T, layer.E, layer.k, layer.S, True, 1024)
+    assert res.best in cands and set(res.ms) == set(cands)
+    assert {kn.ring_rows for kn in cands} == {1024, 512, 256}
+    log("ring tuner: " + ", ".join(f"{k} {v:.3f}" for k, v in list(res.table().items())[:6]))
+    layer.forward()
+    layer.backward()
+    torch.cuda.synchronize()
+    got = _bwd_results(layer)
+    for n, v in ref.items():
+        assert np.array_equal(got[n], v), n
+
+
 def test_kimi_shape_ring_below_peak_load():
     """The Kimi-K2-shaped skewed workload (16,384 tokens, 384 + 1 experts, the hottest expert far
     above the mean) at its own ring capacity of 2,048 rows, below the hottest expert's load:

@@ -78,11 +78,16 @@ def test_apply_sets_and_clears_the_serial_schedule_bit():
 
 def test_ring_candidates_tune_producers_and_keep_whole_slots():
     c = tune.candidates(T=16384, E=384, k=8, n_shared=1, backward=False, ring_rows=2048)
-    assert c[0] == tune.Knobs(256, False, 128)                 # the library default first
+    assert c[0] == tune.Knobs(256, False, 128, 2048)           # the library default first
     assert {kn.producer_wgs for kn in c} == set(tune.PRODUCERS)
-    assert all(2048 % kn.chunk_rows == 0 for kn in c)           # whole slots only
+    assert all(kn.ring_rows % kn.chunk_rows == 0 for kn in c)   # whole slots only
     assert {kn.chunk_rows for kn in c} == {256, 128, 64, 32}
+    assert {kn.ring_rows for kn in c} == {2048, 1024, 512}      # the budget and below, never above
+    assert len(set(c)) == len(c)
     cfg = moe.make_config(16384, 256, 8, 2, 128, ring_rows=2048, flags=moe.MOE_F_RING_DISPATCH)
+    ws = moe.moe_query(cfg)[0]
     tune.apply(cfg, tune.Knobs(128, False, 8))
     assert cfg.chunk_rows == 128 and cfg.producer_wgs == 8 and cfg.ring_rows == 2048
-    moe.moe_query(cfg)
+    for kn in c:   # every candidate runs in the workspace sized for the budget
+        tune.apply(cfg, kn)
+        assert moe.moe_query(cfg)[0] <= ws
