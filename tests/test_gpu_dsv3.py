@@ -201,3 +201,29 @@ def test_bitwise_run_to_run(run):
         assert torch.equal(r, t), name
     del ref
     torch.cuda.empty_cache()
+
+
+def test_ring_dispatch_bitwise_at_full_size(run):
+    """The ring dispatch at its default capacity (16,384 rows: 64 slots, rounds of 32 chunks) and
+    producer count, forward (x rows) and backward (dY rows), on the same experts: every output and
+    gradient bit for bit those of the direct pull."""
+    import torch
+    import mixture_experts_layer_schedule_amd as moe
+    from mixture_experts_layer_schedule_amd import MoeLayer
+    cfg, inp, layer, experts = run
+    ring = MoeLayer.from_config(cfg, with_backward=True, flags=moe.MOE_F_RING_DISPATCH)
+    ring.set_inputs(inp.x_bits, inp.w_r_bits, inp.bias, inp.dy_bits)
+    for a, b in ((ring.w1q, layer.w1q), (ring.w1s, layer.w1s), (ring.w2q, layer.w2q), (ring.w2s, layer.w2s)):
+        a.copy_(b)
+    log("dsv3: forward + backward through the ring")
+    ring.forward()
+    ring.backward()
+    torch.cuda.synchronize()
+    assert moe.moe_device_status(ring.workspace) == 0
+    names = ("y", "y32", "dx", "dx32", "dw_r", "dw1", "dw2")
+    for name in names:
+        assert torch.equal(getattr(ring, name), getattr(layer, name)), name
+    for name in ("g", "u", "hq", "hs", "yslot"):
+        assert torch.equal(ring.saved_tensor(name), layer.saved_tensor(name)), name
+    del ring
+    torch.cuda.empty_cache()
