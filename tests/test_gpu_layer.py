@@ -309,13 +309,15 @@ def test_nonfinite_logits_route_to_valid_experts():
     torch.cuda.synchronize()
 
 
-def test_forward_and_backward_do_not_block_the_host():
+@pytest.mark.parametrize("flags", [0, 2], ids=["direct", "ring"])
+def test_forward_and_backward_do_not_block_the_host(flags):
     """moe_fwd / moe_bwd only enqueue: behind a long-running kernel on the same stream both calls
-    return while the stream is still busy (no host synchronisation inside the layer)."""
+    return while the stream is still busy (no host synchronisation inside the layer), with the
+    direct pull and with the ring dispatch (its rounds ordered by events between two streams)."""
     import time
     import torch
     cfg = moe_inputs.CONFIGS["tiny"].with_(backward=True)
-    layer = gpu_layer(cfg, True)
+    layer = gpu_layer(cfg, True, flags=flags)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     torch.cuda._sleep(200_000_000)   # a bounded spin kernel: tens of milliseconds or more
