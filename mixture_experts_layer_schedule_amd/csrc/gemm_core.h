@@ -1,4 +1,5 @@
-// Core of the grouped MXFP8 GEMMs (shared by the direct kernels and the ring kernel).
+// Core of the grouped MXFP8 GEMMs (shared by the expert GEMM kernels, which also run the ring
+// dispatch rounds, and the persistent ring kernel, which is not launched).
 //
 // Every GEMM here is "NT": both operands are stored with the reduction axis K contiguous and
 // MXFP8-quantised along K (one e8m0 byte per 32 values).  The product runs on
@@ -623,7 +624,7 @@ MOE_DEV uint32_t quant_lane32(float v, uint32_t* scale) {
 MOE_DEV float sigmoid(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 MOE_DEV float silu(float g) { return g * sigmoid(g); }
 
-// Gate/up epilogue shared by the direct and the ring kernels.  For wave w the tile's B rows are
+// Gate/up epilogue (direct and persistent-ring gate/up kernels).  For wave w the tile's B rows are
 // 32 gate rows followed by the 32 matching up rows, so G and U of an element sit in the same
 // lane; h = silu(G) U is quantised along I in 32-column blocks held by the 32 lanes of a
 // half-wave.  n0: first I column of the tile (128 per tile).
