@@ -271,6 +271,8 @@ def main() -> int:
     ap.add_argument("--ring-rows", type=int, default=0,
                     help="ring capacity in rows with --flags 2 (ring dispatch); 0: the workload's own, else 16384")
     ap.add_argument("--producers", type=int, default=0, help="ring producer workgroups (0: 128)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one step captured into a HIP graph (phases from eager steps)")
     ap.add_argument("--no-tune", action="store_true",
                     help="skip the per-workload tuning (chunk_rows 256, backward branch on a second stream)")
     args = ap.parse_args()
@@ -339,27 +341,51 @@ def main() -> int:
     ev = PhaseEvents(len(moe.PHASES))
     moe.moe_set_phase_events(ctypes.addressof(ev.arr), ev.n)
 
-    def step():
-        layer.forward(stream)
+    def step(st=stream):
+        layer.forward(st)
         if not fwd_only:
-            layer.backward(stream)
+            layer.backward(st)
 
     for i in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done")
 
-    def timed(n):
-        """n steps bracketed by events; returns (ms per step, per-phase ms from the library's marks)."""
+    graph = None
+    if args.graph:
+        # one step captured into a HIP graph (no phase marks inside it), after a warm-up step on
+        # a side stream as capture expects
+        moe.moe_set_phase_events(None, 0)
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step(side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        moe.moe_set_phase_events(ctypes.addressof(ev.arr), ev.n)
+        log("[bench] one step captured into a graph")
+
+    def timed(n, replay=False):
+        """n steps (or n replays of the captured step) bracketed by events; returns (ms per step,
+        per-phase ms from the library's marks; zeros for replays)."""
         pms = {p: 0.0 for p in moe.PHASES}
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         total = 0.0
         for i in range(n):
             start.record(stream)
-            step()
+            if replay:
+                graph.replay()
+            else:
+                step()
             stop.record(stream)
             stop.synchronize()
             total += start.elapsed_time(stop)
+            if replay:
+                continue
             prev = None
             for p, name in enumerate(moe.PHASES):
                 if name == "bwd_begin" and fwd_only:
@@ -372,8 +398,13 @@ def main() -> int:
         return total / n, {k: v / n for k, v in pms.items()}
 
     # the timed region: the library's default schedule (backward branch on a second stream)
-    ms, phase_ms_timed = timed(args.steps)
-    log(f"[bench] {args.steps} steps, {ms:.3f} ms/step")
+    if graph is not None:
+        ms, _ = timed(args.steps, replay=True)
+        log(f"[bench] {args.steps} graph replays, {ms:.3f} ms/step")
+        _, phase_ms_timed = timed(min(args.steps, 3))  # the same schedule eagerly: its phase marks
+    else:
+        ms, phase_ms_timed = timed(args.steps)
+        log(f"[bench] {args.steps} steps, {ms:.3f} ms/step")
     if fwd_only or knobs["serial_bwd"]:  # one stream: the phase marks come from the timed region
         ms_serial, phase_ms = ms, phase_ms_timed
     else:
@@ -462,6 +493,7 @@ def main() -> int:
                    "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "inter": cfg.inter, "score": cfg.score,
                    "n_shared": cfg.n_shared, "seed": cfg.seed, "parallelism": "single GPU",
                    "path": "unfused" if args.unfused else ("ring" if ring_kw else "fused"), **knobs,
+                   **({"graph": True} if graph is not None else {}),
                    **({"ring_rows": int(layer.cfg.ring_rows) or 16384} if ring_kw else {})},
         "tuning": tuning,
         "tflops": round(tflops, 2),
