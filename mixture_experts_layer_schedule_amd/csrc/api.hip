@@ -183,17 +183,17 @@ moe_status ensure_init() {
 
 // Extra streams of each device, with fork / join events around their work: kBranchStream runs
 // the backward's independent branch, kRingStream the ring dispatch's producers (its own, so the
-// backward's producers never queue behind that branch).  One set per host thread and device
-// (created on first use, default priority, kept until the process ends), so calls from
-// different threads never share events.
+// backward's producers never queue behind that branch), kRingConsumerStream every other round
+// of the ring's GEMM.  One set per host thread and device (created on first use, default
+// priority, kept until the process ends), so calls from different threads never share events.
 struct SideStream {
   hipStream_t st = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
   bool ok = false, tried = false;
 };
 constexpr int kMaxDevices = 64;
-constexpr int kBranchStream = 0, kRingStream = 1;
-thread_local SideStream t_side[kMaxDevices][2];
+constexpr int kBranchStream = 0, kRingStream = 1, kRingConsumerStream = 2;
+thread_local SideStream t_side[kMaxDevices][3];
 
 // Events that order the ring dispatch's rounds, per host thread and device (created on first
 // use, kept until the process ends).
@@ -286,10 +286,15 @@ struct FwdScratch {
 // dYq).  Chunks (row tiles) go in rounds of H = nslots / 2, chunk c in slot c % nslots.  Round
 // r's gather (producers on the ring stream) waits for the GEMM of round r - lag, the last round
 // whose chunks used its slots (lag = nslots / H, so the rounds in between use others); round r's
-// GEMM, launched by consume(chunk0, nchunks) on the caller's stream, waits for its gather.  The
-// host bounds the chunk count by tiles_bound; rounds past the schedule's real count find no
-// chunks and return.  Without overlap (or without the ring stream) everything runs in launch
-// order on the caller's stream.
+// GEMM, launched by consume(chunk0, nchunks, stream), waits for its gather.  With lag >= 2 the
+// GEMM rounds alternate between the caller's stream and a consumer stream of the library's, so
+// that two rounds' GEMMs (on disjoint slots) share the GPU; the caller's stream waits for the
+// consumer stream's last round at the end.  While the caller's stream is being captured into a
+// graph the GEMM rounds all stay on the caller's stream: the capture of a step whose rounds used
+// both consumer streams ended the process (DeepSeek-V3 shape; cause not found), and the
+// one-consumer schedule captures and replays bit for bit.  The host bounds the chunk count by
+// tiles_bound; rounds past the schedule's real count find no chunks and return.  Without
+// overlap (or without the ring stream) everything runs in launch order on the caller's stream.
 template <class Consume>
 moe_status ring_rounds(const Dims& m, const SchedView& sv, const uint8_t* q, const uint8_t* qs, uint8_t* ring,
                        uint8_t* ring_s, bool overlap, hipStream_t stream, Consume consume) {
@@ -297,26 +302,38 @@ moe_status ring_rounds(const Dims& m, const SchedView& sv, const uint8_t* q, con
   const int lag = nslots / H;
   const int rounds = (int)((m.tiles_bound + H - 1) / H);
   SideStream* side = overlap ? side_stream(kRingStream) : nullptr;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  bool capturing = true;  // when the query fails: the schedule that is known to capture
+  if (hipStreamIsCapturing(stream, &cap) == hipSuccess) capturing = cap != hipStreamCaptureStatusNone;
+  else (void)hipGetLastError();  // leave no error behind for the launch checks
+  SideStream* cons2 = side && lag >= 2 && !capturing ? side_stream(kRingConsumerStream) : nullptr;
   int dev = 0;
   MOE_TRY(hipGetDevice(&dev));
   RingEvents& ev = t_ring_events[dev % kMaxDevices];
   const size_t K = (size_t)lag + 2;  // event r % K is recorded again only after round r - lag's wait
   if (side && !ev.ensure(K)) return MOE_ELAUNCH;
   hipStream_t ps = side ? side->st : stream;
+  const hipStream_t cs[2] = {stream, cons2 ? cons2->st : stream};
   if (side) {
     MOE_TRY(hipEventRecord(side->fork, stream));  // the pulled rows and the schedule are ready
     MOE_TRY(hipStreamWaitEvent(ps, side->fork, 0));
+    if (cons2) MOE_TRY(hipStreamWaitEvent(cs[1], side->fork, 0));
   }
   for (int r = 0; r < rounds; ++r) {
+    const hipStream_t c = cs[r & 1];
     if (side && r >= lag) MOE_TRY(hipStreamWaitEvent(ps, ev.cons[(r - lag) % K], 0));
     MOE_TRY(launch_ring_gather(sv, q, qs, (int)m.d, ring, ring_s, (int)m.tile_rows, nslots, r * H, H,
                                (int)m.producers, ps));
     if (side) {
       MOE_TRY(hipEventRecord(ev.prod[r % K], ps));
-      MOE_TRY(hipStreamWaitEvent(stream, ev.prod[r % K], 0));
+      MOE_TRY(hipStreamWaitEvent(c, ev.prod[r % K], 0));
     }
-    MOE_TRY(consume(r * H, H));
-    if (side) MOE_TRY(hipEventRecord(ev.cons[r % K], stream));
+    MOE_TRY(consume(r * H, H, c));
+    if (side) MOE_TRY(hipEventRecord(ev.cons[r % K], c));
+  }
+  if (cons2) {  // the consumer stream's rounds are all done before the caller's next kernel
+    MOE_TRY(hipEventRecord(cons2->join, cs[1]));
+    MOE_TRY(hipStreamWaitEvent(stream, cons2->join, 0));
   }
   return MOE_OK;
 }
@@ -433,11 +450,12 @@ moe_status forward_impl(const moe_config* cfg, const Dims& m, const moe_saved_la
     ga.nslots = (int)m.nslots;
     ga.slot_rows = (int)m.tile_rows;
     moe_status st;
-    if ((st = ring_rounds(m, sv, xq, xs, sc.ring, sc.ring_s, true, stream, [&](int chunk0, int nchunks) {
-           ga.chunk0 = chunk0;
-           ga.nchunks = nchunks;
-           return launch_gemm_gateup(ga, nchunks, stream);
-         })) != MOE_OK)
+    if ((st = ring_rounds(m, sv, xq, xs, sc.ring, sc.ring_s, true, stream,
+                          [&](int chunk0, int nchunks, hipStream_t cst) {
+                            ga.chunk0 = chunk0;
+                            ga.nchunks = nchunks;
+                            return launch_gemm_gateup(ga, nchunks, cst);
+                          })) != MOE_OK)
       return st;
   }
   mark(stream, MOE_PH_GATEUP);
@@ -660,10 +678,11 @@ moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const v
     dd.nslots = (int)m.nslots;
     dd.slot_rows = (int)m.tile_rows;
     if ((st = ring_rounds(m, sv, dyq, dys, at<uint8_t>(workspace, wl.ring), at<uint8_t>(workspace, wl.ring_s),
-                          !(cfg->flags & MOE_F_SERIAL_BWD), stream, [&](int chunk0, int nchunks) {
+                          !(cfg->flags & MOE_F_SERIAL_BWD), stream,
+                          [&](int chunk0, int nchunks, hipStream_t cst) {
                             dd.chunk0 = chunk0;
                             dd.nchunks = nchunks;
-                            return launch_gemm_dgrad_down(dd, nchunks, stream);
+                            return launch_gemm_dgrad_down(dd, nchunks, cst);
                           })) != MOE_OK)
       return st;
   }
