@@ -27,20 +27,36 @@ __global__ __launch_bounds__(256) void k_permute_rows(SchedView s, const uint8_t
   for (int c = threadIdx.x; c < d / 128; c += blockDim.x) ds[c] = ss[c];
 }
 
-// H = silu(G) U quantised along I in blocks of 32 columns (one block per half-wave): the
-// fused gate/up epilogue's arithmetic on G and U read back from HBM.
+// H = silu(G) U quantised along I in blocks of 32 columns: the fused gate/up epilogue's
+// arithmetic on G and U read back from HBM.  Each lane takes 4 consecutive columns (16-byte loads
+// of G and U, one 4-byte store of their codes), so a block is 8 lanes and its maximum a 3-step
+// exchange among them; every value goes through the same scaling and conversion as in the
+// epilogue, so the codes are the same bits.
 __global__ __launch_bounds__(256) void k_swiglu_quant(const float* __restrict__ g, const float* __restrict__ u, int I,
                                                       uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
   const int r = blockIdx.x;
-  const int n = blockIdx.y * blockDim.x + threadIdx.x;
-  // past I (whole 32-column blocks, I % 32 == 0) the lanes repeat the last column so that every
-  // lane of a block takes part in its maximum; they store nothing
-  const size_t o = (size_t)r * I + min(n, I - 1);
-  uint32_t sc;
-  const uint32_t code = quant_lane32(silu(g[o]) * u[o], &sc);
-  if (n < I) {
-    hq[o] = (uint8_t)code;
-    if ((n & 31) == 0) hs[(size_t)r * (I / 32) + (n >> 5)] = (uint8_t)sc;
+  const int n = blockIdx.y * blockDim.x + threadIdx.x;  // 4-column group of the row
+  const int n4 = I / 4;
+  // past I (whole 8-lane blocks, I % 32 == 0) the lanes repeat the last group: they store nothing
+  const size_t o = (size_t)r * I + 4 * (size_t)min(n, n4 - 1);
+  const v4f gv = *(const v4f*)(g + o), uv = *(const v4f*)(u + o);
+  // the block maximum on the bit patterns of |h|, as the epilogue takes it (a NaN wins there too)
+  float h[4];
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    h[j] = silu(gv[j]) * uv[j];
+    m = max(m, __float_as_uint(fabsf(h[j])));
+  }
+#pragma unroll
+  for (int x = 1; x < 8; x <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, x));
+  const uint32_t byte = e8m0_from_amax(__uint_as_float(m));
+  const float inv = e8m0_inv_scale(byte);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(h[0] * inv), clamp448(h[1] * inv), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(h[2] * inv), clamp448(h[3] * inv), w, true);
+  if (n < n4) {
+    *(uint32_t*)(hq + o) = (uint32_t)w;
+    if ((n & 7) == 0) hs[(size_t)r * (I / 32) + (n >> 3)] = (uint8_t)byte;
   }
 }
 
@@ -65,7 +81,7 @@ hipError_t launch_permute_rows(const SchedView& s, const uint8_t* xq, const uint
 hipError_t launch_swiglu_quant(const float* g, const float* u, int RS, int I, uint8_t* hq, uint8_t* hs,
                                hipStream_t st) {
   if (RS == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_swiglu_quant, dim3(RS, (I + 255) / 256), dim3(256), 0, st, g, u, I, hq, hs);
+  hipLaunchKernelGGL(k_swiglu_quant, dim3(RS, (I / 4 + 255) / 256), dim3(256), 0, st, g, u, I, hq, hs);
   return hipGetLastError();
 }
 
