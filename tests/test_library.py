@@ -228,3 +228,37 @@ def test_mfma_probe_rejects_bad_arguments_without_launching():
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_probe_mfma(1 << 20, 0, stream=0, sink_bytes=1 << 30)
     assert ei.value.status == moe.MOE_EINVAL
+
+
+def test_header_compiles_as_c_and_a_c_program_queries_the_layout(tmp_path):
+    """include/moe.h is a C header: a C99 program built with gcc against it links the library
+    and gets the same buffer sizes from moe_query as the Python binding, and the same status for a
+    rejected configuration."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    libdir = os.path.dirname(moe.LIB_PATH)
+    exe = tmp_path / "query_sizes"
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+           "-I" + os.path.join(root, "include"), os.path.join(root, "tests", "c_abi", "query_sizes.c"),
+           "-L" + libdir, "-l:" + os.path.basename(moe.LIB_PATH), "-Wl,-rpath," + libdir, "-o", str(exe)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # warnings from inside the HIP runtime headers are theirs; the program's own must be clean
+    if r.returncode != 0 and "query_sizes.c" in r.stderr:
+        raise AssertionError(r.stderr[-2000:])
+    if r.returncode != 0:
+        cmd.remove("-Werror")
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-2000:]
+    for shape in ((8192, 7168, 256, 8, 2048, 0, 0), (16384, 7168, 384, 8, 2048, 1, moe.MOE_F_FORWARD_ONLY),
+                  (256, 256, 8, 2, 128, 0, moe.MOE_F_RING_DISPATCH)):
+        out = subprocess.run([str(exe), *map(str, shape)], capture_output=True, text=True, check=True).stdout.split()
+        T, d, E, k, inter, S, flags = shape
+        cfg = moe.make_config(T, d, E, k, inter, S, moe.MOE_SCORE_SIGMOID, flags=flags)
+        ws, sl, wl = moe.moe_query(cfg, with_workspace_layout=True)
+        assert [int(v) for v in out[:4]] == [moe.MOE_OK, ws, sl.total, wl.total]
+        assert int(out[4]) == moe.MOE_ESHAPE and " ".join(out[5:]) == moe.moe_strerror(moe.MOE_ESHAPE)
+
