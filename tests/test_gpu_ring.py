@@ -8,7 +8,9 @@ import numpy as np
 import pytest
 
 import moe_inputs
-from helpers import log, to_np
+from helpers import EMPTY, K1_SHARED, MAX_ROUTE, ONE_TOKEN, RAGGED, log, to_np
+
+EDGE = {c.name: c for c in (ONE_TOKEN, EMPTY, MAX_ROUTE, K1_SHARED, RAGGED)}
 
 pytestmark = pytest.mark.gpu
 
@@ -124,6 +126,23 @@ def test_backward_ring_matches_direct_pull(bwd_ref, ring_rows, producers, serial
     cfg, inp, ws, ref = bwd_ref
     flags = RING | (moe.MOE_F_SERIAL_BWD if serial else 0)
     got = _bwd_results(_run_bwd(cfg, inp, ws, ring_rows=ring_rows, producer_wgs=producers, flags=flags))
+    for n, v in ref.items():
+        assert np.array_equal(got[n], v), n
+
+
+@pytest.mark.parametrize("cfg", [EDGE[n] for n in ("one_token", "empty_experts", "max_route", "k1_shared", "ragged")],
+                         ids=lambda c: c.name)
+@pytest.mark.parametrize("ring_rows", [256, 512])
+def test_ring_on_edge_layers(cfg, ring_rows):
+    """The edge layers (one token, experts with no rows, E = 512 with k = 16, k = 1 plus a shared
+    expert, ragged tails) through a one-slot and a two-slot ring, forward and backward: every
+    output, gradient and [dG dU] bit for bit those of the direct pull."""
+    import mixture_experts_layer_schedule_amd as moe
+    cfg = cfg.with_(backward=True)
+    inp = moe_inputs.layer_inputs(cfg)
+    ws = [moe_inputs.expert_weights(cfg, e) for e in range(cfg.E + cfg.n_shared)]
+    ref = _bwd_results(_run_bwd(cfg, inp, ws, flags=moe.MOE_F_DIRECT_GATHER))
+    got = _bwd_results(_run_bwd(cfg, inp, ws, ring_rows=ring_rows, flags=RING))
     for n, v in ref.items():
         assert np.array_equal(got[n], v), n
 
