@@ -214,9 +214,10 @@ def cpu_baseline(cfg, inp, n_experts: int, backward: bool = True) -> dict:
         dyq, dys = oracle.quantize(inp.dy.astype(np.float64), axis=1)
         DY = oracle.dequantize(dyq, dys, axis=1)
     t_dense = time.perf_counter() - t0
-    # expert sample: experts with the median load
-    order = np.argsort(sched.counts)
-    sample = [int(e) for e in order[len(order) // 2: len(order) // 2 + n_experts]]
+    # expert sample: experts at evenly spaced quantiles of the load (low to high)
+    order = np.argsort(sched.counts, kind="stable")
+    n_experts = max(1, min(n_experts, len(order)))
+    sample = [int(order[(2 * i + 1) * len(order) // (2 * n_experts)]) for i in range(n_experts)]
     t_exp = 0.0
     rows = 0
     for e in sample:
@@ -240,7 +241,7 @@ def cpu_baseline(cfg, inp, n_experts: int, backward: bool = True) -> dict:
         "value": cfg.T / t_total, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
         "sample": (f"float64 NumPy oracle: router, top-k, schedule and activation quantisation on all {cfg.T} "
                    f"tokens ({t_dense:.1f} s) + expert {what} on {len(sample)} "
-                   f"median-load experts ({rows} rows, {t_exp:.1f} s), scaled by routed rows "
+                   f"experts at evenly spaced load quantiles ({rows} rows, {t_exp:.1f} s), scaled by routed rows "
                    f"{cfg.T * cfg.k}/{rows}; estimated layer time {t_total:.1f} s"),
         **res,
     }
@@ -257,7 +258,7 @@ def main() -> int:
     ap.add_argument("--tokens", type=int, default=0,
                     help="override the workload's token count T (a T sweep; the default workload is unchanged)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-experts", type=int, default=2)
+    ap.add_argument("--cpu-experts", type=int, default=8)
     ap.add_argument("--dominant", default="auto", help="phase reported in roofline (default: longest)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (scales HBM byte counters)")
