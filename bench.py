@@ -38,9 +38,10 @@ def log(*a):
 # and once out per stage, dW once, the dense E-times work not counted.  R = T*k routed rows,
 # NX experts; weights are MXFP8 (1 byte + 1/32 scale byte per value); activations as stored.
 
-def phase_work(cfg, tok_pad: int, backward: bool = True) -> dict:
+def phase_work(cfg, tok_pad: int, backward: bool = True, dw_bytes: int = 4) -> dict:
     """With ``backward`` the forward GEMMs also write the weights requantised along the other axis
-    (W1^T, W2^T: the dgrad GEMMs' operands), once per weight byte."""
+    (W1^T, W2^T: the dgrad GEMMs' operands), once per weight byte.  dw_bytes: bytes per weight
+    gradient element (4, or 2 with MOE_F_DW_BF16)."""
     T, d, E, k, I, S = cfg.T, cfg.d, cfg.E, cfg.k, cfg.inter, cfg.n_shared
     NX, R = E + S, T * cfg.k + S * T
     q = 1 + 1 / 32  # MXFP8 bytes per value
@@ -60,8 +61,8 @@ def phase_work(cfg, tok_pad: int, backward: bool = True) -> dict:
         "dgrad_gateup": (2.0 * R * 2 * I * d, w1 + R * 2 * I * q + R * d * 4),
         "dx_reduce": (0.0, R * d * 4 + T * d * 6),
         "token_requant": (0.0, (R * (2 * d + 3 * I) * q) + tok_pad * (2 * d + 3 * I) * q),
-        "wgrad_down": (2.0 * R * d * I, NX * d * I * 4 + tok_pad * (d + I) * q),
-        "wgrad_gateup": (2.0 * R * 2 * I * d, NX * 2 * I * d * 4 + tok_pad * (2 * I + d) * q),
+        "wgrad_down": (2.0 * R * d * I, NX * d * I * dw_bytes + tok_pad * (d + I) * q),
+        "wgrad_gateup": (2.0 * R * 2 * I * d, NX * 2 * I * d * dw_bytes + tok_pad * (2 * I + d) * q),
     }
 
 
@@ -272,6 +273,8 @@ def main() -> int:
     ap.add_argument("--ring-rows", type=int, default=0,
                     help="ring capacity in rows with --flags 2 (ring dispatch); 0: the workload's own, else 16384")
     ap.add_argument("--producers", type=int, default=0, help="ring producer workgroups (0: 128)")
+    ap.add_argument("--dw-bf16", action="store_true",
+                    help="weight gradients in bf16 (MOE_F_DW_BF16); the default writes them in float32")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one step captured into a HIP graph (phases from eager steps)")
     ap.add_argument("--no-tune", action="store_true",
@@ -295,7 +298,8 @@ def main() -> int:
     cfg = moe_inputs.CONFIGS[args.config].with_(backward=not fwd_only)
     if args.tokens:
         cfg = cfg.with_(T=args.tokens, name=f"{cfg.name}_T{args.tokens}")
-    flags = args.flags | (moe.MOE_F_FORWARD_ONLY if fwd_only else 0) | (moe.MOE_F_UNFUSED if args.unfused else 0)
+    flags = (args.flags | (moe.MOE_F_FORWARD_ONLY if fwd_only else 0) | (moe.MOE_F_UNFUSED if args.unfused else 0)
+             | (moe.MOE_F_DW_BF16 if args.dw_bf16 else 0))
     t0 = time.time()
     inp = moe_inputs.layer_inputs(cfg, with_dy=not fwd_only)
     ring_kw = {}
@@ -423,7 +427,7 @@ def main() -> int:
         return 1
 
     tok_off = layer.saved_tensor("tok_off").cpu().numpy()
-    work = phase_work(cfg, int(tok_off[-1]), backward=not fwd_only)
+    work = phase_work(cfg, int(tok_off[-1]), backward=not fwd_only, dw_bytes=2 if flags & moe.MOE_F_DW_BF16 else 4)
     # the grouped GEMMs' work items: row tiles (up to 256 rows of one expert) x column tiles
     counts = layer.saved_tensor("counts").cpu().numpy()
     row_tiles = int(layer.saved_tensor("tile_start").cpu().numpy()[-1])
@@ -459,7 +463,7 @@ def main() -> int:
         roof = {"bound": "hbm", "achieved": round(b / t / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     # the committed counters were taken on the default workload only
-    default_run = args.config == "dsv3_fwd_bwd" and not args.tokens and not fwd_only
+    default_run = args.config == "dsv3_fwd_bwd" and not args.tokens and not fwd_only and not args.dw_bf16
     roof["traffic"] = measured_traffic(dom, ring=bool(args.flags & 2)) if default_run else None
     roof["kernel"] = dom
     roof["timed_in"] = "timed region" if clean else "launch-order pass"
@@ -495,6 +499,7 @@ def main() -> int:
                    "n_shared": cfg.n_shared, "seed": cfg.seed, "parallelism": "single GPU",
                    "path": "unfused" if args.unfused else ("ring" if ring_kw else "fused"), **knobs,
                    **({"graph": True} if graph is not None else {}),
+                   **({"dw": "bf16"} if args.dw_bf16 else {}),
                    **({"ring_rows": int(layer.cfg.ring_rows) or 16384} if ring_kw else {})},
         "tuning": tuning,
         "tflops": round(tflops, 2),

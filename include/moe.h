@@ -139,6 +139,13 @@ typedef struct moe_config {
  * moe_fwd_noalloc rejects it (MOE_EINVAL). */
 #define MOE_F_UNFUSED 32u
 
+/* Weight gradients in bfloat16: moe_bwd writes dw1 and dw2 as bf16 (2 bytes per element, same
+ * shapes and layouts), each the round-to-nearest-even of the float32 value the default path
+ * writes, bit for bit.  The fp32 weight gradients are most of the backward's HBM traffic (the
+ * byte floor of the DeepSeek-V3-shape layer drops by about a quarter); callers that keep their
+ * gradient accumulation elsewhere can take them in bf16.  moe_fwd ignores it. */
+#define MOE_F_DW_BF16 64u
+
 /* Byte offsets inside the caller-owned `saved` buffer that moe_fwd fills and moe_bwd reads
  * (the schedule is built once and reused by the backward pass: knowledge card, 方法/产品要点).
  * R = T*k routed rows, RS = R + n_shared*T rows in expert-major ("permuted") order,
@@ -269,14 +276,14 @@ moe_status moe_fwd_noalloc(const moe_config* cfg, const void* x, const void* w_r
  * reverse-dispatch, schedule reused; article "Cursor 為 Composer 改造 MoE 訓練…", section
  * "2.37 倍同 1.41 倍係兩份成績": the layer's backward).  The expert weights enter through their
  * transposes in `saved`.  Outputs: dx_bf16 [T, d] and dx_f32 [T, d] float (or NULL);
- * dw_router [E, d] float; dw1 [NX, 2I, d] float and dw2 [NX, d, I] float (same layouts as
- * w1q / w2q).
+ * dw_router [E, d] float; dw1 [NX, 2I, d] and dw2 [NX, d, I] (same layouts as w1q / w2q), float,
+ * or bf16 with MOE_F_DW_BF16.
  * Steps: quantise dy; combine-weight and router gradients; dgrad of the down GEMM (rows pulled
  * from dy: reverse-combine) with the SwiGLU backward and quantisation along 2I; dgrad of the
  * gate/up GEMM pushing rows to their (token, slot) (reverse-dispatch); fixed-order reduction of
  * dx; token-axis requantisation of the wgrad operands; weight-gradient GEMMs. */
 moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const void* w_router, const void* saved,
-                   size_t saved_bytes, void* dx_bf16, float* dx_f32, float* dw_router, float* dw1, float* dw2,
+                   size_t saved_bytes, void* dx_bf16, float* dx_f32, float* dw_router, void* dw1, void* dw2,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Phase timing, for measurement only (the pages attribute the layer's time to its phases:

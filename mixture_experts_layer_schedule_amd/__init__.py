@@ -21,6 +21,7 @@ MOE_F_SERIAL_BWD = 4
 MOE_F_IDENTITY_EXPERTS = 8
 MOE_F_FORWARD_ONLY = 16
 MOE_F_UNFUSED = 32
+MOE_F_DW_BF16 = 64
 MOE_DEV_RING_TIMEOUT, MOE_DEV_NONFINITE_LOGIT = 1, 2
 
 # every symbol include/moe.h declares

@@ -48,7 +48,7 @@ Dims dims(const moe_config& c) {
 
 constexpr uint32_t kKnownFlags =
     MOE_F_DIRECT_GATHER | MOE_F_RING_DISPATCH | MOE_F_SERIAL_BWD | MOE_F_IDENTITY_EXPERTS | MOE_F_FORWARD_ONLY |
-    MOE_F_UNFUSED;
+    MOE_F_UNFUSED | MOE_F_DW_BF16;
 
 moe_status check_config(const moe_config* c) {
   if (!c) return MOE_EINVAL;
@@ -569,7 +569,7 @@ moe_status moe_fwd_noalloc(const moe_config* cfg, const void* x, const void* w_r
 }
 
 moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const void* w_router, const void* saved,
-                   size_t saved_bytes, void* dx_bf16, float* dx_f32, float* dw_router, float* dw1, float* dw2,
+                   size_t saved_bytes, void* dx_bf16, float* dx_f32, float* dw_router, void* dw1, void* dw2,
                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
@@ -615,6 +615,7 @@ moe_status moe_bwd(const moe_config* cfg, const void* dy, const void* x, const v
   const int tb = (int)m.tile64_bound;
   WgradArgs wa{};
   wa.tok_off = tok_off;
+  wa.dw_bf16 = (cfg->flags & MOE_F_DW_BF16) ? 1 : 0;
   wa.ld = m.ld_tok;
   auto side_branch = [&]() -> moe_status {
     ta.q = at<uint8_t>(saved, sl.xq); ta.qs = at<uint8_t>(saved, sl.xs); ta.cols = d; ta.src = TOK_X;

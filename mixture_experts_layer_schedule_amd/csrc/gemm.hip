@@ -371,7 +371,21 @@ __global__ __launch_bounds__(512, 1) void k_gemm_wgrad(WgradArgs p) {
   v16f acc[FH][2];
   mainloop8<kWgradF>(lds, L, K / KS, acc);
   if (!active) return;
-  float* out = p.dw + (size_t)e * p.M * p.N;
+  if (p.dw_bf16) {
+    // the same float32 values rounded to bf16: half the bytes of the store stream, non-temporal
+    // like the float32 ones (the two fragments write the two halves of each row's 128-byte line)
+    uint16_t* out = (uint16_t*)p.dw + (size_t)e * p.M * p.N;
+    static_for<FH>([&]<int mi>() {
+      static_for<16>([&]<int v>() {
+        const int m = m0 + 32 * (mh + mi) + 8 * (v >> 2) + 4 * h + (v & 3);
+        uint16_t* dst = out + (size_t)m * p.N + n0 + 64 * wc + i;
+        __builtin_nontemporal_store(f32_to_bf16(acc[mi][0][v]), dst);
+        __builtin_nontemporal_store(f32_to_bf16(acc[mi][1][v]), dst + 32);
+      });
+    });
+    return;
+  }
+  float* out = (float*)p.dw + (size_t)e * p.M * p.N;
   static_for<FH>([&]<int mi>() {
     static_for<16>([&]<int v>() {
       const int m = m0 + 32 * (mh + mi) + 8 * (v >> 2) + 4 * h + (v & 3);

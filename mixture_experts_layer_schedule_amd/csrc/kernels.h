@@ -66,9 +66,10 @@ struct DgradGateUpArgs {
 struct WgradArgs {
   const uint8_t *at, *ats, *bt, *bts;  // [M][ld], [M][ld/32]; [N][ld], [N][ld/32]
   const int64_t* tok_off;              // [n_exp + 1] padded token offsets (multiples of 128)
-  float* dw;                           // [n_exp][M][N]
+  void* dw;                            // [n_exp][M][N] float, or bf16 with dw_bf16
   int64_t ld;
   int M, N, n_exp;                     // M a multiple of 128
+  int dw_bf16;                         // store dw rounded to bf16 (nearest, ties to even)
 };
 
 // Persistent gate/up kernel fed through ring token buffers (producer / consumer workgroups).

@@ -4,7 +4,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (MOE_SCORE_SIGMOID, MOE_SCORE_SOFTMAX, make_config, moe_bwd, moe_fwd, moe_query,
+from . import (MOE_F_DW_BF16, MOE_SCORE_SIGMOID, MOE_SCORE_SOFTMAX, make_config, moe_bwd, moe_fwd, moe_query,
                moe_quantize_mxfp8)
 
 
@@ -38,8 +38,9 @@ class MoeLayer:
             self.dx = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
             self.dx32 = torch.empty((T, d), dtype=torch.float32, device=dev)
             self.dw_r = torch.empty((E, d), dtype=torch.float32, device=dev)
-            self.dw1 = torch.empty((NX, 2 * I, d), dtype=torch.float32, device=dev)
-            self.dw2 = torch.empty((NX, d, I), dtype=torch.float32, device=dev)
+            dwt = torch.bfloat16 if flags & MOE_F_DW_BF16 else torch.float32
+            self.dw1 = torch.empty((NX, 2 * I, d), dtype=dwt, device=dev)
+            self.dw2 = torch.empty((NX, d, I), dtype=dwt, device=dev)
 
     @classmethod
     def from_config(cls, cfg, **kw):

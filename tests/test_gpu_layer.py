@@ -218,6 +218,24 @@ def test_serial_and_concurrent_backward_identical(pair):
         assert torch.equal(a, b), name
 
 
+def test_bf16_weight_gradients_are_the_rounded_float32_ones(pair):
+    """MOE_F_DW_BF16 writes dW1 and dW2 in bf16: each element is the float32 gradient of the
+    default path rounded to nearest, ties to even, bit for bit; dx and dW_router are unchanged."""
+    import torch
+    import mixture_experts_layer_schedule_amd as moe
+    cfg, inp, fw, bw, layer = pair
+    layer.forward()
+    layer.backward()
+    torch.cuda.synchronize()
+    ws = [moe_inputs.expert_weights(cfg, e) for e in range(cfg.E + cfg.n_shared)]
+    b16 = gpu_layer(cfg, True, inp=inp, ws=ws, flags=moe.MOE_F_DW_BF16)
+    assert b16.dw1.dtype == torch.bfloat16 and b16.dw2.dtype == torch.bfloat16
+    for name, a, b in (("dW1", layer.dw1, b16.dw1), ("dW2", layer.dw2, b16.dw2)):
+        assert torch.equal(a.to(torch.bfloat16).view(torch.int16), b.view(torch.int16)), name
+    for name, a, b in (("dx", layer.dx32, b16.dx32), ("dW_r", layer.dw_r, b16.dw_r)):
+        assert torch.equal(a, b), name
+
+
 @pytest.mark.parametrize("rows", [32, 96, 128])
 def test_row_tile_height_changes_no_bit(pair, rows):
     """chunk_rows (rows per GEMM row tile, the tuning knob of the direct path) changes the work

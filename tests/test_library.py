@@ -111,7 +111,7 @@ def test_forward_only_layout_drops_transposed_weights():
     (dict(flags=2, chunk_rows=128, ring_rows=192), moe.MOE_ESHAPE),
     (dict(flags=2, producer_wgs=129), moe.MOE_ESHAPE),
     (dict(flags=3), moe.MOE_EINVAL),         # direct gather and ring dispatch together
-    (dict(flags=64), moe.MOE_EINVAL),        # unknown flag
+    (dict(flags=128), moe.MOE_EINVAL),       # unknown flag
     (dict(flags=32), moe.MOE_EINVAL),        # the unfused forward needs MOE_F_FORWARD_ONLY
     (dict(flags=32 | 16 | 8), moe.MOE_EINVAL),  # ... and real experts
     # the unfused forward's permuted rows: T * (k + S) * d reaches 2^32
@@ -261,4 +261,14 @@ def test_header_compiles_as_c_and_a_c_program_queries_the_layout(tmp_path):
         ws, sl, wl = moe.moe_query(cfg, with_workspace_layout=True)
         assert [int(v) for v in out[:4]] == [moe.MOE_OK, ws, sl.total, wl.total]
         assert int(out[4]) == moe.MOE_ESHAPE and " ".join(out[5:]) == moe.moe_strerror(moe.MOE_ESHAPE)
+
+
+def test_flag_values_match_the_header():
+    """Every MOE_F_* flag the header defines has the same value in the binding, and moe_query
+    accepts each one that stands alone on the default path (bf16 weight gradients included)."""
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    flags = {n: int(v) for n, v in re.findall(r"#define (MOE_F_\w+) (\d+)u", text)}
+    assert flags and all(getattr(moe, n) == v for n, v in flags.items())
+    for f in (moe.MOE_F_DW_BF16, moe.MOE_F_DW_BF16 | moe.MOE_F_RING_DISPATCH | moe.MOE_F_SERIAL_BWD):
+        moe.moe_query(moe.make_config(4096, 256, 8, 2, 128, flags=f))
 
