@@ -23,8 +23,9 @@
  *     moe_status; nothing is launched then.  Launch failures return MOE_ELAUNCH.
  *   - Tensor pointers must be 16-byte aligned; `saved` and `workspace` 256-byte aligned.
  *   - Concurrency: calls on different streams may overlap as long as they use different
- *     `saved` and `workspace` buffers.  moe_set_phase_events is process-wide and meant for
- *     single-threaded measurement.
+ *     `saved` and `workspace` buffers; the library's own streams and the events that order
+ *     them are kept per host thread and device, so calls from different threads never share
+ *     them.  moe_set_phase_events is process-wide and meant for single-threaded measurement.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -49,7 +50,9 @@ typedef enum moe_status {
 
 /* Codes the device writes into the workspace status word (read with moe_device_status).  The
  * word is sticky: a later call does not clear it. */
-#define MOE_DEV_RING_TIMEOUT 1   /* a bounded wait of the ring dispatch kernel expired */
+#define MOE_DEV_RING_TIMEOUT 1   /* a bounded wait of the persistent ring kernel expired (that
+                                    kernel is not launched; the stream-ordered ring of
+                                    MOE_F_RING_DISPATCH has no device-side waits) */
 #define MOE_DEV_NONFINITE_LOGIT 2 /* a router logit was NaN or infinite (its token is still
                                      routed to k distinct valid experts; NaN ranks as -inf) */
 
