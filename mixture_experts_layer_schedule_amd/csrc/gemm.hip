@@ -364,23 +364,32 @@ __global__ __launch_bounds__(512, 1) void k_gemm_wgrad(WgradArgs p) {
   const uint8_t* bt = p.bt + (size_t)n0 * ld + k0;
   const uint8_t* ats = p.ats + (size_t)m0 * (ld / 32) + k0 / 32;
   const uint8_t* bts = p.bts + (size_t)n0 * (ld / 32) + k0 / 32;
+  // With bf16 weight gradients the B rows are staged in pair order: in each wave's 64 columns,
+  // fragment 0's lane i computes column 2i and fragment 1's lane i column 2i + 1, so that a lane
+  // packs two neighbouring bf16 values into one word (the same dot products, other labels).
+  // float32 keeps the plain order: 4-byte stores of 32 neighbouring columns fill a line already.
+  const bool pairs = p.dw_bf16 != 0;
+  auto bcol = [&](int r) {
+    const int j = r & 63;
+    return pairs ? (r & ~63) + (j < 32 ? 2 * j : 2 * (j - 32) + 1) : r;
+  };
   L.init(at, [&](int r) { return at + (size_t)min(r, 32 * kWgradF - 1) * ld; },
-         bt, [&](int r) { return bt + (size_t)(min(n0 + r, p.N - 1) - n0) * ld; },
+         bt, [&](int r) { return bt + (size_t)(min(n0 + bcol(r), p.N - 1) - n0) * ld; },
          ats, [&](int r) { return ats + (size_t)min(r, 32 * kWgradF - 1) * (ld / 32); },
-         bts, [&](int r) { return bts + (size_t)(min(n0 + r, p.N - 1) - n0) * (ld / 32); });
+         bts, [&](int r) { return bts + (size_t)(min(n0 + bcol(r), p.N - 1) - n0) * (ld / 32); });
   v16f acc[FH][2];
   mainloop8<kWgradF>(lds, L, K / KS, acc);
   if (!active) return;
-  if (p.dw_bf16) {
-    // the same float32 values rounded to bf16: half the bytes of the store stream, non-temporal
-    // like the float32 ones (the two fragments write the two halves of each row's 128-byte line)
+  if (pairs) {
+    // the same float32 values rounded to bf16: half the bytes of the store stream; lane i writes
+    // columns 2i, 2i + 1 as one word, so each half-wave writes one whole 128-byte line
     uint16_t* out = (uint16_t*)p.dw + (size_t)e * p.M * p.N;
     static_for<FH>([&]<int mi>() {
       static_for<16>([&]<int v>() {
         const int m = m0 + 32 * (mh + mi) + 8 * (v >> 2) + 4 * h + (v & 3);
-        uint16_t* dst = out + (size_t)m * p.N + n0 + 64 * wc + i;
-        __builtin_nontemporal_store(f32_to_bf16(acc[mi][0][v]), dst);
-        __builtin_nontemporal_store(f32_to_bf16(acc[mi][1][v]), dst + 32);
+        const uint32_t word =
+            (uint32_t)f32_to_bf16(acc[mi][0][v]) | ((uint32_t)f32_to_bf16(acc[mi][1][v]) << 16);
+        __builtin_nontemporal_store(word, (uint32_t*)(out + (size_t)m * p.N + n0 + 64 * wc + 2 * i));
       });
     });
     return;
